@@ -1,0 +1,173 @@
+/*
+ * gqla.h -- C ABI of libgqla: GQLA (Group-Query Latent Attention) decode
+ * attention for AMD Instinct MI355X (gfx950).
+ *
+ * Method: "GQLA: Group-Query Latent Attention for Hardware-Adaptive Large
+ * Language Model Decoding" (arXiv 2605.15250).  One set of group-indexed
+ * latent weights (W_UK[G], W_UV[G], G < g) exposes two algebraically
+ * equivalent decode paths (paperlayer.ai summary, section 3 "Methods", bullet
+ * "Two equivalent decoding paths"; gist.science technical summary, section 2
+ * "Architektur"):
+ *   - the MQA-absorb path: W_UK[G] folded into each query head, attention of
+ *     all h_q heads over the shared latent cache (c^KV_t ++ k^R_t), output
+ *     up-projected by W_UV[G];
+ *   - the GQA path: the latent cache expanded once into g K/V groups plus the
+ *     shared rope key; conventional grouped-query attention with s_q query
+ *     tokens per sequence (multi-token prediction) and no per-step expansion.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *   never allocates, frees or retains them and never synchronises.  Every
+ *   call only enqueues kernels on `stream` (a hipStream_t passed as void*;
+ *   NULL = the null stream) and returns.
+ * - bf16 tensors are passed as void* to 16-bit bfloat16 storage; fp32 as
+ *   float*; indices as int32_t*.  Every tensor pointer must be 16-byte
+ *   aligned and densely packed in the row-major shape given.
+ * - Head h belongs to group G = h / (h_q / g).  W_UK[G] is (d_latent x d_nope)
+ *   and W_UV[G] is (d_latent x d_v): the key/value of token t in group G are
+ *   the row vectors c_t W_UK[G] and c_t W_UV[G].
+ * - Logits are (q_nope . k_nope + q_rope . k_rope) * softmax_scale.  q_rope
+ *   and k_rope arrive already rotated.
+ * - cache_seqlens[b] = L_b counts the s_q new tokens; query row i < s_q of
+ *   sequence b sees cache tokens t <= L_b - s_q + i (causal mask between the
+ *   MTP rows).  Precondition: s_q <= L_b.
+ * - Paged cache: token t of sequence b is slot t % block_size of page
+ *   block_table[b * max_blocks + t / block_size].  Only entries t / block_size
+ *   < ceil(L_b / block_size) are read.  Precondition: those entries are valid
+ *   page indices.
+ * - lse outputs are natural-log sum-exp of the scaled logits (fp32).
+ * - Split-KV: split_offsets (device, int32 [batch + 1], prefix sums) gives
+ *   sequence b the splits split_offsets[b] .. split_offsets[b+1]-1; split j
+ *   of b covers tokens [j*split_tokens, min((j+1)*split_tokens, L_b)).
+ *   split_tokens must be a positive multiple of block_size and
+ *   split_offsets[batch] must equal total_splits (caller's duty: use
+ *   ceil(L_b / split_tokens) splits for sequence b).  Partials are the
+ *   normalised attention output over the split and its lse; a split in which
+ *   a row sees no token holds out = 0, lse = -inf.
+ * - Errors: a negative return value means nothing was enqueued.  Argument
+ *   checks happen on the host before any HIP call, so they never touch the
+ *   device.  GQLA_ERR_HIP reports a launch failure (hipGetLastError).
+ *   Calls are reentrant (no mutable global state); calls on different
+ *   streams may overlap.
+ *
+ * Supported shapes (compile-time instantiations; others return
+ * GQLA_ERR_UNSUPPORTED_SHAPE): block_size = 64, s_q in {1, 2}, and
+ *   (h_q/g, d_latent, d_rope, d_nope, d_v) in
+ *     {(16, 512, 64, 128, 128), (4, 512, 64, 128, 128), (8, 64, 16, 32, 32)}.
+ */
+#ifndef GQLA_H
+#define GQLA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GQLA_OK 0
+#define GQLA_ERR_INVALID_ARG (-1)
+#define GQLA_ERR_UNSUPPORTED_SHAPE (-2)
+#define GQLA_ERR_MISALIGNED (-3)
+#define GQLA_ERR_BAD_SPLIT_PLAN (-4)
+#define GQLA_ERR_HIP (-5)
+
+/* Problem dimensions, in the pages' notation (paperlayer.ai section 3
+ * "Architecture": h_q heads, g groups of per-head dim d_h, latent c^KV_t,
+ * per-head q^R_h and shared k^R; s_q query tokens per step). */
+typedef struct gqla_dims {
+    int32_t num_heads;     /* h_q */
+    int32_t num_groups;    /* g: number of distinct W_UK[G] / W_UV[G] */
+    int32_t d_latent;      /* r_kv: latent width of c^KV_t */
+    int32_t d_rope;        /* d^R_h: shared decoupled-RoPE key width */
+    int32_t d_nope;        /* per-head K-NoPE width */
+    int32_t d_v;           /* per-head V width */
+    int32_t s_q;           /* query tokens per sequence per step (1 + MTP heads) */
+    int32_t block_size;    /* tokens per cache page */
+    float softmax_scale;   /* 0 => 1/sqrt(d_nope + d_rope) */
+} gqla_dims;
+
+/* Elements per page of each cache format.
+ * Latent page:   [block_size][d_latent + d_rope]   (c_t ++ k_rope_t per slot;
+ *                576 elements = 1152 B per token for the DeepSeek-V3 shape,
+ *                paperlayer.ai section 5 "Conversion setup").
+ * Expanded page: for G in 0..g-1: K block [block_size][d_nope] then V block
+ *                [d_v][block_size] (dim-major); then rope [block_size][d_rope].
+ *                2*g*d_h + d_rope elements per token (same passage; 4224 B per
+ *                token at g = 8, section 4 "GQA path"). */
+int64_t gqla_latent_page_elems(const gqla_dims* d);
+int64_t gqla_expanded_page_elems(const gqla_dims* d);
+
+/* One-shot cache expansion (latent -> per-group K/V), the deployment-time
+ * switch to the GQA path (paperlayer.ai section 3, "Two equivalent decoding
+ * paths": a one-shot cache compression or expansion; pwwt.cn section 3).
+ *   latent_pages   bf16 [num_pages][block_size][d_latent + d_rope]
+ *   w_uk           bf16 [g][d_latent][d_nope]
+ *   w_uv           bf16 [g][d_latent][d_v]
+ *   page_ids       int32 [num_pages_to_expand] or NULL (= pages 0..num_pages-1)
+ *   expanded_pages bf16 [num_pages][gqla_expanded_page_elems]; page p of the
+ *                  output corresponds to latent page p, so one block table
+ *                  indexes both caches.
+ * Every slot of each listed page is expanded: K = RNE_bf16(c W_UK[G]),
+ * V = RNE_bf16(c W_UV[G]) with fp32 accumulation; the rope key is copied
+ * bit-exactly. */
+int gqla_expand_cache(const gqla_dims* d, const void* latent_pages, const void* w_uk,
+                      const void* w_uv, int64_t num_pages, const int32_t* page_ids,
+                      int64_t num_pages_to_expand, void* expanded_pages, void* stream);
+
+/* MQA-absorb decode over the latent cache (paperlayer.ai section 4,
+ * "MQA-absorb path"; gist.science section 2 "MQA-Absorb-Pfad"):
+ *   q_abs = W_UK[G] q_nope,  s_t = (q_abs . c_t + q_rope . k_rope_t) * scale,
+ *   o_lat = softmax(s) C,     out = o_lat W_UV[G].
+ *   q_nope  bf16 [batch][s_q][h_q][d_nope]     q_rope bf16 [batch][s_q][h_q][d_rope]
+ *   latent_pages as for gqla_expand_cache; block_table int32 [batch][max_blocks];
+ *   cache_seqlens int32 [batch]; w_uk, w_uv as for gqla_expand_cache.
+ *   split_offsets   NULL => one split per sequence (no partials touched), else the
+ *                   split plan described above.
+ *   out      bf16 [batch][s_q][h_q][d_v] or NULL.  With a split plan and out != NULL
+ *            the merge (gqla_splitkv_combine) is enqueued after the decode.
+ *   lse      fp32 [batch][s_q][h_q] or NULL.
+ *   part_out fp32 [total_splits][s_q][h_q][d_v], part_lse fp32 [total_splits][s_q][h_q]:
+ *            required iff split_offsets != NULL.  W_UV[G] is applied per split
+ *            (exact by linearity), so partials are in the output space. */
+int gqla_decode_mqa_absorb(const gqla_dims* d, int32_t batch, const void* q_nope,
+                           const void* q_rope, const void* latent_pages,
+                           const int32_t* block_table, int32_t max_blocks,
+                           const int32_t* cache_seqlens, const void* w_uk, const void* w_uv,
+                           const int32_t* split_offsets, int32_t split_tokens,
+                           int32_t total_splits, void* out, float* lse, float* part_out,
+                           float* part_lse, void* stream);
+
+/* GQA decode over the per-group expanded cache (paperlayer.ai section 4,
+ * "GQA path"; gist.science section 2 "GQA-Pfad": conventional grouped-query
+ * attention with no per-step latent expansion).  Arguments as for
+ * gqla_decode_mqa_absorb, with expanded_pages (bf16 [num_pages]
+ * [gqla_expanded_page_elems]) in place of the latent cache and no weights. */
+int gqla_decode_gqa(const gqla_dims* d, int32_t batch, const void* q_nope, const void* q_rope,
+                    const void* expanded_pages, const int32_t* block_table, int32_t max_blocks,
+                    const int32_t* cache_seqlens, const int32_t* split_offsets,
+                    int32_t split_tokens, int32_t total_splits, void* out, float* lse,
+                    float* part_out, float* part_lse, void* stream);
+
+/* Log-sum-exp merge of split partials (the pages are silent on split-KV; this
+ * is the exact decomposition of a softmax over disjoint token ranges):
+ *   m = max_s lse_s, w_s = exp(lse_s - m), out = sum_s w_s o_s / sum_s w_s
+ *   (rounded to bf16), lse = m + log(sum_s w_s).  Splits with lse = -inf carry
+ *   weight 0; a row whose splits are all empty gets out = 0, lse = -inf.
+ *   part_out fp32 [total_splits][s_q][h_q][d_v], part_lse fp32 [total_splits][s_q][h_q],
+ *   out bf16 [batch][s_q][h_q][d_v], lse fp32 [batch][s_q][h_q] or NULL. */
+int gqla_splitkv_combine(const gqla_dims* d, int32_t batch, const int32_t* split_offsets,
+                         int32_t total_splits, const float* part_out, const float* part_lse,
+                         void* out, float* lse, void* stream);
+
+/* Human-readable text for a status code (static storage; never NULL). */
+const char* gqla_status_string(int status);
+
+/* ABI version (major * 100 + minor). */
+int gqla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQLA_H */
