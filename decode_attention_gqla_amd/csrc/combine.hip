@@ -1,0 +1,66 @@
+// Split-KV log-sum-exp merge.
+//
+// The GQLA pages do not discuss splitting the context; the merge is the exact
+// decomposition of a softmax over disjoint token ranges: with per-split
+// normalised outputs o_s and log-sum-exps lse_s,
+//   m = max_s lse_s,  w_s = exp(lse_s - m),
+//   out = sum_s w_s o_s / sum_s w_s,   lse = m + log(sum_s w_s).
+// Splits with lse = -inf (no visible token) carry weight 0.
+//
+// One thread per 4 consecutive output dims of one (sequence, row); a row of
+// d_v dims is d_v/4 adjacent threads, so every split partial row is read with
+// fully coalesced 16-byte loads.
+#include "common.hip.h"
+#include "params.hip.h"
+
+namespace gqla {
+
+template <int DV>
+__global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
+  constexpr int TPR = DV / 4;                      // threads per row
+  const int tid = blockIdx.x * 256 + threadIdx.x;
+  const int gr = tid / TPR;                         // global row = b * rows + r
+  const int part = tid % TPR;
+  if (gr >= p.batch * p.rows) return;
+  const int b = gr / p.rows, r = gr % p.rows;
+  const int s0 = p.split_offsets[b], s1 = p.split_offsets[b + 1];
+
+  float m = -INFINITY;
+  for (int s = s0; s < s1; ++s) m = fmaxf(m, p.part_lse[(size_t)s * p.rows + r]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float z = 0.f;
+  if (m != -INFINITY) {
+    for (int s = s0; s < s1; ++s) {
+      const float ls = p.part_lse[(size_t)s * p.rows + r];
+      if (ls == -INFINITY) continue;
+      const float w = expf(ls - m);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(p.part_out + ((size_t)s * p.rows + r) * DV + 4 * part);
+      acc += w * v;
+      z += w;
+    }
+  }
+  const float inv = z > 0.f ? 1.f / z : 0.f;
+  const f32x4 o = acc * inv;
+  u32x2 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+  *reinterpret_cast<u32x2*>(p.out + (size_t)gr * DV + 4 * part) = pk;
+  if (part == 0 && p.lse) p.lse[gr] = z > 0.f ? m + logf(z) : -INFINITY;
+}
+
+hipError_t combine_dispatch(int dv, const CombineParams& p, hipStream_t stream, bool* supported) {
+  *supported = true;
+  const long threads_per_row = dv / 4;
+  const long total = (long)p.batch * p.rows * threads_per_row;
+  const unsigned grid = (unsigned)((total + 255) / 256);
+  if (grid == 0) return hipSuccess;
+  if (dv == 128) {
+    hipLaunchKernelGGL(combine_kernel<128>, dim3(grid), dim3(256), 0, stream, p);
+  } else if (dv == 32) {
+    hipLaunchKernelGGL(combine_kernel<32>, dim3(grid), dim3(256), 0, stream, p);
+  } else {
+    *supported = false;
+    return hipSuccess;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gqla

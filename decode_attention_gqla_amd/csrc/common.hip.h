@@ -1,0 +1,89 @@
+// Shared device helpers for the GQLA kernels (gfx950 / CDNA4, wave64).
+//
+// MFMA operand layouts used throughout (v_mfma_f32_16x16x32_bf16), for a
+// lane l = 16*q + c (q = l/16 in 0..3, c = l%16):
+//   A (16 x 32, m x k):  lane holds A[m = c][k = 8q .. 8q+7]
+//   B (32 x 16, k x n):  lane holds B[k = 8q .. 8q+7][n = c]
+//   D (16 x 16, m x n):  lane holds D[m = 4q .. 4q+3][n = c]
+// The k order inside an instruction is shared by A and B, so any consistent
+// relabelling of k (e.g. of cache tokens) leaves the product unchanged.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f2bf_bits(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f2bf_bits(lo) | ((uint32_t)f2bf_bits(hi) << 16);
+}
+
+__device__ __forceinline__ float bf_bits2f(uint32_t bits16) {
+  return __builtin_bit_cast(float, bits16 << 16);
+}
+
+// 16-byte global load straight into an MFMA operand register quad.
+__device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+}
+
+// Zero the bf16 elements j >= keep of an 8-element operand (0 <= keep <= 8).
+__device__ __forceinline__ bf16x8 keep_first(const bf16x8& v, int keep) {
+  u32x4 u = __builtin_bit_cast(u32x4, v);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int j = 2 * w;
+    uint32_t m = (j < keep ? 0x0000ffffu : 0u) | (j + 1 < keep ? 0xffff0000u : 0u);
+    u[w] &= m;
+  }
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+__device__ __forceinline__ float wave_max_xor16_32(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  v = fmaxf(v, __shfl_xor(v, 32, 64));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum_xor16_32(float v) {
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+// Find the sequence owning split w: largest b with split_offsets[b] <= w.
+__device__ __forceinline__ int split_owner(const int32_t* __restrict__ offs, int batch, int w) {
+  int lo = 0, hi = batch - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (offs[mid] <= w) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+}  // namespace gqla

@@ -1,0 +1,254 @@
+// C ABI of libgqla: argument validation on the host, then kernel dispatch.
+// Every check runs before the first HIP call, so a rejected call enqueues
+// nothing and never touches the device.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/gqla.h"
+#include "common.hip.h"
+#include "params.hip.h"
+
+namespace gqla {
+hipError_t gqa_dispatch(int hpg, int sq, int dn, int dv, int dr, const DecodeParams& p,
+                        hipStream_t stream, bool* supported);
+hipError_t absorb_dispatch(int hpg, int sq, int r, int dn, int dv, int dr, const DecodeParams& p,
+                           hipStream_t stream, bool* supported);
+hipError_t expand_dispatch(int r, int dn, int dv, int dr, const ExpandParams& p, hipStream_t stream,
+                           bool* supported);
+hipError_t combine_dispatch(int dv, const CombineParams& p, hipStream_t stream, bool* supported);
+}  // namespace gqla
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+// The shapes compiled into this library.
+bool shape_supported(const gqla_dims* d) {
+  const int hpg = d->num_heads / d->num_groups;
+  if (d->block_size != 64 || (d->s_q != 1 && d->s_q != 2)) return false;
+  if (d->d_latent == 512 && d->d_rope == 64 && d->d_nope == 128 && d->d_v == 128)
+    return hpg == 16 || hpg == 4;
+  if (d->d_latent == 64 && d->d_rope == 16 && d->d_nope == 32 && d->d_v == 32) return hpg == 8;
+  return false;
+}
+
+int check_dims(const gqla_dims* d) {
+  if (!d) return GQLA_ERR_INVALID_ARG;
+  if (d->num_heads <= 0 || d->num_groups <= 0 || d->d_latent <= 0 || d->d_rope < 0 ||
+      d->d_nope <= 0 || d->d_v <= 0 || d->s_q <= 0 || d->block_size <= 0)
+    return GQLA_ERR_INVALID_ARG;
+  if (d->num_heads % d->num_groups != 0) return GQLA_ERR_INVALID_ARG;
+  if (!(isfinite(d->softmax_scale)) || d->softmax_scale < 0.f) return GQLA_ERR_INVALID_ARG;
+  if (!shape_supported(d)) return GQLA_ERR_UNSUPPORTED_SHAPE;
+  return GQLA_OK;
+}
+
+float scale_of(const gqla_dims* d) {
+  return d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / sqrtf((float)(d->d_nope + d->d_rope));
+}
+
+// Shared checks of the two decode entry points.  cache/w_uk/w_uv are checked
+// by the caller (the GQA path has no weights).
+int check_decode(const gqla_dims* d, int32_t batch, const void* q_nope, const void* q_rope,
+                 const void* cache, const int32_t* block_table, int32_t max_blocks,
+                 const int32_t* seqlens, const int32_t* split_offsets, int32_t split_tokens,
+                 int32_t total_splits, const void* out, const float* lse, const float* part_out,
+                 const float* part_lse) {
+  int st = check_dims(d);
+  if (st != GQLA_OK) return st;
+  if (batch < 0 || max_blocks <= 0) return GQLA_ERR_INVALID_ARG;
+  if (!q_nope || !q_rope || !cache || !block_table || !seqlens) return GQLA_ERR_INVALID_ARG;
+  if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(cache) || !aligned4(block_table) ||
+      !aligned4(seqlens))
+    return GQLA_ERR_MISALIGNED;
+  if (split_offsets) {
+    if (split_tokens <= 0 || split_tokens % d->block_size != 0 || total_splits < batch)
+      return GQLA_ERR_BAD_SPLIT_PLAN;
+    if (!aligned4(split_offsets)) return GQLA_ERR_MISALIGNED;
+    if (!part_out || !part_lse) return GQLA_ERR_INVALID_ARG;
+    if (!aligned16(part_out) || !aligned4(part_lse)) return GQLA_ERR_MISALIGNED;
+  } else {
+    if (!out) return GQLA_ERR_INVALID_ARG;
+  }
+  if (out && !aligned16(out)) return GQLA_ERR_MISALIGNED;
+  if (lse && !aligned4(lse)) return GQLA_ERR_MISALIGNED;
+  return GQLA_OK;
+}
+
+gqla::DecodeParams make_params(const gqla_dims* d, int32_t batch, const void* q_nope,
+                               const void* q_rope, const void* cache, const int32_t* block_table,
+                               int32_t max_blocks, const int32_t* seqlens, const void* w_uk,
+                               const void* w_uv, const int32_t* split_offsets,
+                               int32_t split_tokens, int32_t total_splits, void* out, float* lse,
+                               float* part_out, float* part_lse) {
+  gqla::DecodeParams p;
+  p.q_nope = (const uint16_t*)q_nope;
+  p.q_rope = (const uint16_t*)q_rope;
+  p.cache = (const uint16_t*)cache;
+  p.block_table = block_table;
+  p.seqlens = seqlens;
+  p.w_uk = (const uint16_t*)w_uk;
+  p.w_uv = (const uint16_t*)w_uv;
+  p.split_offsets = split_offsets;
+  p.out = (uint16_t*)out;
+  p.lse = lse;
+  p.part_out = part_out;
+  p.part_lse = part_lse;
+  p.batch = batch;
+  p.max_blocks = max_blocks;
+  p.num_groups = d->num_groups;
+  p.split_tokens = split_offsets ? split_tokens : 0;
+  p.num_units = split_offsets ? total_splits : batch;
+  p.scale_log2 = scale_of(d) * gqla::kLog2e;
+  p.qcat = nullptr;
+  return p;
+}
+
+int finish(hipError_t e, bool supported) {
+  if (!supported) return GQLA_ERR_UNSUPPORTED_SHAPE;
+  return e == hipSuccess ? GQLA_OK : GQLA_ERR_HIP;
+}
+
+int enqueue_combine(const gqla_dims* d, int32_t batch, const int32_t* split_offsets,
+                    const float* part_out, const float* part_lse, void* out, float* lse,
+                    hipStream_t stream) {
+  gqla::CombineParams c;
+  c.part_out = part_out;
+  c.part_lse = part_lse;
+  c.split_offsets = split_offsets;
+  c.out = (uint16_t*)out;
+  c.lse = lse;
+  c.batch = batch;
+  c.rows = d->s_q * d->num_heads;
+  bool ok = true;
+  hipError_t e = gqla::combine_dispatch(d->d_v, c, stream, &ok);
+  return finish(e, ok);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gqla_abi_version(void) { return 100; }
+
+const char* gqla_status_string(int status) {
+  switch (status) {
+    case GQLA_OK: return "GQLA_OK";
+    case GQLA_ERR_INVALID_ARG: return "GQLA_ERR_INVALID_ARG: null pointer, bad dimension or inconsistent argument";
+    case GQLA_ERR_UNSUPPORTED_SHAPE: return "GQLA_ERR_UNSUPPORTED_SHAPE: no kernel instantiated for these dimensions";
+    case GQLA_ERR_MISALIGNED: return "GQLA_ERR_MISALIGNED: tensor pointers must be 16-byte aligned (index arrays 4-byte)";
+    case GQLA_ERR_BAD_SPLIT_PLAN: return "GQLA_ERR_BAD_SPLIT_PLAN: split_tokens must be a positive multiple of block_size and total_splits >= batch";
+    case GQLA_ERR_HIP: return "GQLA_ERR_HIP: kernel launch failed";
+    default: return "unknown gqla status";
+  }
+}
+
+int64_t gqla_latent_page_elems(const gqla_dims* d) {
+  if (!d) return -1;
+  return (int64_t)d->block_size * (d->d_latent + d->d_rope);
+}
+
+int64_t gqla_expanded_page_elems(const gqla_dims* d) {
+  if (!d) return -1;
+  return (int64_t)d->block_size * ((int64_t)d->num_groups * (d->d_nope + d->d_v) + d->d_rope);
+}
+
+uint64_t gqla_mqa_absorb_workspace_bytes(const gqla_dims* d, int32_t batch) {
+  if (!d || batch <= 0 || d->s_q <= 0 || d->num_heads <= 0 || d->d_latent <= 0 || d->d_rope < 0)
+    return 0;
+  return (uint64_t)batch * d->s_q * d->num_heads * (uint64_t)(d->d_latent + d->d_rope) * 2u;
+}
+
+int gqla_expand_cache(const gqla_dims* d, const void* latent_pages, const void* w_uk,
+                      const void* w_uv, int64_t num_pages, const int32_t* page_ids,
+                      int64_t num_pages_to_expand, void* expanded_pages, void* stream) {
+  int st = check_dims(d);
+  if (st != GQLA_OK) return st;
+  if (num_pages < 0 || num_pages_to_expand < 0) return GQLA_ERR_INVALID_ARG;
+  if (!page_ids && num_pages_to_expand > num_pages) return GQLA_ERR_INVALID_ARG;
+  if (num_pages_to_expand == 0) return GQLA_OK;
+  if (!latent_pages || !w_uk || !w_uv || !expanded_pages) return GQLA_ERR_INVALID_ARG;
+  if (!aligned16(latent_pages) || !aligned16(w_uk) || !aligned16(w_uv) ||
+      !aligned16(expanded_pages) || (page_ids && !aligned4(page_ids)))
+    return GQLA_ERR_MISALIGNED;
+  gqla::ExpandParams p;
+  p.latent = (const uint16_t*)latent_pages;
+  p.w_uk = (const uint16_t*)w_uk;
+  p.w_uv = (const uint16_t*)w_uv;
+  p.page_ids = page_ids;
+  p.expanded = (uint16_t*)expanded_pages;
+  p.n_expand = num_pages_to_expand;
+  p.num_groups = d->num_groups;
+  bool ok = true;
+  hipError_t e = gqla::expand_dispatch(d->d_latent, d->d_nope, d->d_v, d->d_rope, p,
+                                       (hipStream_t)stream, &ok);
+  return finish(e, ok);
+}
+
+int gqla_decode_mqa_absorb(const gqla_dims* d, int32_t batch, const void* q_nope,
+                           const void* q_rope, const void* latent_pages,
+                           const int32_t* block_table, int32_t max_blocks,
+                           const int32_t* cache_seqlens, const void* w_uk, const void* w_uv,
+                           const int32_t* split_offsets, int32_t split_tokens,
+                           int32_t total_splits, void* out, float* lse, float* part_out,
+                           float* part_lse, void* workspace, uint64_t workspace_bytes,
+                           void* stream) {
+  int st = check_decode(d, batch, q_nope, q_rope, latent_pages, block_table, max_blocks,
+                        cache_seqlens, split_offsets, split_tokens, total_splits, out, lse,
+                        part_out, part_lse);
+  if (st != GQLA_OK) return st;
+  if (!w_uk || !w_uv) return GQLA_ERR_INVALID_ARG;
+  if (!aligned16(w_uk) || !aligned16(w_uv)) return GQLA_ERR_MISALIGNED;
+  if (batch == 0) return GQLA_OK;
+  if (!workspace || workspace_bytes < gqla_mqa_absorb_workspace_bytes(d, batch))
+    return GQLA_ERR_INVALID_ARG;
+  if (!aligned16(workspace)) return GQLA_ERR_MISALIGNED;
+  gqla::DecodeParams p = make_params(d, batch, q_nope, q_rope, latent_pages, block_table,
+                                     max_blocks, cache_seqlens, w_uk, w_uv, split_offsets,
+                                     split_tokens, total_splits, out, lse, part_out, part_lse);
+  p.qcat = (uint16_t*)workspace;
+  bool ok = true;
+  hipError_t e = gqla::absorb_dispatch(d->num_heads / d->num_groups, d->s_q, d->d_latent,
+                                       d->d_nope, d->d_v, d->d_rope, p, (hipStream_t)stream, &ok);
+  st = finish(e, ok);
+  if (st != GQLA_OK || !split_offsets || !out) return st;
+  return enqueue_combine(d, batch, split_offsets, part_out, part_lse, out, lse, (hipStream_t)stream);
+}
+
+int gqla_decode_gqa(const gqla_dims* d, int32_t batch, const void* q_nope, const void* q_rope,
+                    const void* expanded_pages, const int32_t* block_table, int32_t max_blocks,
+                    const int32_t* cache_seqlens, const int32_t* split_offsets,
+                    int32_t split_tokens, int32_t total_splits, void* out, float* lse,
+                    float* part_out, float* part_lse, void* stream) {
+  int st = check_decode(d, batch, q_nope, q_rope, expanded_pages, block_table, max_blocks,
+                        cache_seqlens, split_offsets, split_tokens, total_splits, out, lse,
+                        part_out, part_lse);
+  if (st != GQLA_OK) return st;
+  if (batch == 0) return GQLA_OK;
+  gqla::DecodeParams p = make_params(d, batch, q_nope, q_rope, expanded_pages, block_table,
+                                     max_blocks, cache_seqlens, nullptr, nullptr, split_offsets,
+                                     split_tokens, total_splits, out, lse, part_out, part_lse);
+  bool ok = true;
+  hipError_t e = gqla::gqa_dispatch(d->num_heads / d->num_groups, d->s_q, d->d_nope, d->d_v,
+                                    d->d_rope, p, (hipStream_t)stream, &ok);
+  st = finish(e, ok);
+  if (st != GQLA_OK || !split_offsets || !out) return st;
+  return enqueue_combine(d, batch, split_offsets, part_out, part_lse, out, lse, (hipStream_t)stream);
+}
+
+int gqla_splitkv_combine(const gqla_dims* d, int32_t batch, const int32_t* split_offsets,
+                         int32_t total_splits, const float* part_out, const float* part_lse,
+                         void* out, float* lse, void* stream) {
+  int st = check_dims(d);
+  if (st != GQLA_OK) return st;
+  if (batch < 0 || total_splits < 0) return GQLA_ERR_INVALID_ARG;
+  if (batch == 0) return GQLA_OK;
+  if (!split_offsets || !part_out || !part_lse || !out) return GQLA_ERR_INVALID_ARG;
+  if (!aligned4(split_offsets) || !aligned16(part_out) || !aligned4(part_lse) || !aligned16(out) ||
+      (lse && !aligned4(lse)))
+    return GQLA_ERR_MISALIGNED;
+  return enqueue_combine(d, batch, split_offsets, part_out, part_lse, out, lse, (hipStream_t)stream);
+}
+
+}  // extern "C"

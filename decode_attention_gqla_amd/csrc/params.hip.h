@@ -1,0 +1,49 @@
+// Kernel parameter blocks (plain structs passed by value to the kernels).
+#pragma once
+#include <stdint.h>
+
+namespace gqla {
+
+struct DecodeParams {
+  const uint16_t* q_nope;        // [B][s_q][h_q][d_nope]
+  const uint16_t* q_rope;        // [B][s_q][h_q][d_rope]
+  const uint16_t* cache;         // latent or expanded pages
+  const int32_t* block_table;    // [B][max_blocks]
+  const int32_t* seqlens;        // [B]
+  const uint16_t* w_uk;          // [g][r][d_nope]   (absorb path only)
+  const uint16_t* w_uv;          // [g][r][d_v]      (absorb path only)
+  const int32_t* split_offsets;  // [B+1] or nullptr
+  uint16_t* qcat;                // absorb path: [B][s_q][h_q][r + d_rope] workspace
+  uint16_t* out;                 // [B][s_q][h_q][d_v] bf16 (unsplit launch)
+  float* lse;                    // [B][s_q][h_q] or nullptr (unsplit launch)
+  float* part_out;               // [S][s_q][h_q][d_v] (split launch)
+  float* part_lse;               // [S][s_q][h_q]      (split launch)
+  int32_t batch;
+  int32_t max_blocks;
+  int32_t num_groups;
+  int32_t split_tokens;          // tokens per split (split launch)
+  int32_t num_units;             // total splits, or batch when unsplit
+  float scale_log2;              // softmax scale * log2(e)
+};
+
+struct ExpandParams {
+  const uint16_t* latent;        // [n_pages][bs][r + d_rope]
+  const uint16_t* w_uk;          // [g][r][d_nope]
+  const uint16_t* w_uv;          // [g][r][d_v]
+  const int32_t* page_ids;       // [n] or nullptr
+  uint16_t* expanded;            // [n_pages][page_elems]
+  int64_t n_expand;              // pages to expand
+  int32_t num_groups;
+};
+
+struct CombineParams {
+  const float* part_out;         // [S][rows][d_v]
+  const float* part_lse;         // [S][rows]
+  const int32_t* split_offsets;  // [B+1]
+  uint16_t* out;                 // [B][rows][d_v]
+  float* lse;                    // [B][rows] or nullptr
+  int32_t batch;
+  int32_t rows;                  // s_q * h_q
+};
+
+}  // namespace gqla

@@ -129,14 +129,24 @@ int gqla_expand_cache(const gqla_dims* d, const void* latent_pages, const void* 
  *   lse      fp32 [batch][s_q][h_q] or NULL.
  *   part_out fp32 [total_splits][s_q][h_q][d_v], part_lse fp32 [total_splits][s_q][h_q]:
  *            required iff split_offsets != NULL.  W_UV[G] is applied per split
- *            (exact by linearity), so partials are in the output space. */
+ *            (exact by linearity), so partials are in the output space.
+ *   workspace  device scratch of at least gqla_mqa_absorb_workspace_bytes(d, batch)
+ *            bytes, 16-byte aligned, owned by the caller; it receives the
+ *            absorbed queries [batch][s_q][h_q][d_latent + d_rope] (bf16) and must
+ *            not be shared by calls that may run concurrently.  Too small or NULL
+ *            returns GQLA_ERR_INVALID_ARG. */
 int gqla_decode_mqa_absorb(const gqla_dims* d, int32_t batch, const void* q_nope,
                            const void* q_rope, const void* latent_pages,
                            const int32_t* block_table, int32_t max_blocks,
                            const int32_t* cache_seqlens, const void* w_uk, const void* w_uv,
                            const int32_t* split_offsets, int32_t split_tokens,
                            int32_t total_splits, void* out, float* lse, float* part_out,
-                           float* part_lse, void* stream);
+                           float* part_lse, void* workspace, uint64_t workspace_bytes,
+                           void* stream);
+
+/* Bytes of device workspace gqla_decode_mqa_absorb needs for `batch` sequences
+ * (0 for batch <= 0 or d == NULL). */
+uint64_t gqla_mqa_absorb_workspace_bytes(const gqla_dims* d, int32_t batch);
 
 /* GQA decode over the per-group expanded cache (paperlayer.ai section 4,
  * "GQA path"; gist.science section 2 "GQA-Pfad": conventional grouped-query

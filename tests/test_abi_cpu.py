@@ -1,0 +1,143 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the header
+declares, and rejects bad arguments on the host before any HIP call (so these
+calls are safe with fake device pointers)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+import decode_attention_gqla_amd as G
+from decode_attention_gqla_amd import Dims
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqla.h")
+OK, INVALID, UNSUPPORTED, MISALIGNED, BADSPLIT = 0, -1, -2, -3, -4
+A = ctypes.c_void_p(0x10000)     # fake, 16-byte aligned "device" pointers: never dereferenced
+B_ = ctypes.c_void_p(0x20000)
+ODD = ctypes.c_void_p(0x10002)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(G.LIB_PATH):
+        from decode_attention_gqla_amd import build
+        build.build()
+    return G.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(gqla_\w+)\s*\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) >= {"gqla_expand_cache", "gqla_decode_mqa_absorb", "gqla_decode_gqa",
+                          "gqla_splitkv_combine", "gqla_status_string"}
+    nm = subprocess.run(["nm", "-D", "--defined-only", G.LIB_PATH], capture_output=True, text=True)
+    exported = set(re.findall(r"\bT (gqla_\w+)", nm.stdout))
+    for n in names:
+        assert n in exported, n
+        assert getattr(lib, n) is not None
+
+
+def dsv3(s_q=1, **kw):
+    d = Dims.make(128, 8, 512, 64, 128, 128, s_q)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def absorb(lib, d, batch=1, q=A, split=None, split_tokens=0, total=0, out=A, part=(None, None),
+           ws=A, ws_bytes=1 << 40):
+    return lib.gqla_decode_mqa_absorb(ctypes.byref(d) if d is not None else None, batch, q, A, A,
+                                      A, 4, A, A, A, split, split_tokens, total, out, None,
+                                      part[0], part[1], ws, ws_bytes, None)
+
+
+def gqa(lib, d, batch=1, q=A, split=None, split_tokens=0, total=0, out=A, part=(None, None)):
+    return lib.gqla_decode_gqa(ctypes.byref(d) if d is not None else None, batch, q, A, A, A, 4,
+                               A, split, split_tokens, total, out, None, part[0], part[1], None)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.gqla_abi_version() >= 100
+    for st in (OK, INVALID, UNSUPPORTED, MISALIGNED, BADSPLIT, -5, 7):
+        assert isinstance(G.gqla_status_string(st), str)
+    assert "MISALIGNED" in G.gqla_status_string(MISALIGNED)
+
+
+def test_page_sizes(lib):
+    d = dsv3()
+    assert lib.gqla_latent_page_elems(ctypes.byref(d)) == 64 * 576
+    assert lib.gqla_expanded_page_elems(ctypes.byref(d)) == 64 * 2112
+    d4 = Dims.make(128, 4, 512, 64, 128, 128, 1)
+    assert lib.gqla_expanded_page_elems(ctypes.byref(d4)) == 64 * 1088
+
+
+@pytest.mark.parametrize("call", [absorb, gqa])
+def test_decode_argument_errors_return_before_any_launch(lib, call):
+    assert call(lib, None) == INVALID
+    assert call(lib, dsv3(num_heads=127)) == INVALID                 # h_q % g != 0
+    assert call(lib, dsv3(num_heads=96)) == UNSUPPORTED               # 12 heads per group
+    assert call(lib, dsv3(block_size=32)) == UNSUPPORTED
+    assert call(lib, dsv3(s_q=3)) == UNSUPPORTED
+    assert call(lib, dsv3(d_rope=32)) == UNSUPPORTED
+    assert call(lib, dsv3(softmax_scale=float("nan"))) == INVALID
+    assert call(lib, dsv3(), batch=-1) == INVALID
+    assert call(lib, dsv3(), q=None) == INVALID
+    assert call(lib, dsv3(), q=ODD) == MISALIGNED
+    assert call(lib, dsv3(), out=None) == INVALID                     # unsplit needs out
+    assert call(lib, dsv3(), out=ODD) == MISALIGNED
+    # split plans
+    assert call(lib, dsv3(), split=A, split_tokens=100, total=4, part=(A, B_)) == BADSPLIT
+    assert call(lib, dsv3(), split=A, split_tokens=0, total=4, part=(A, B_)) == BADSPLIT
+    assert call(lib, dsv3(), batch=4, split=A, split_tokens=1024, total=2, part=(A, B_)) == BADSPLIT
+    assert call(lib, dsv3(), split=A, split_tokens=1024, total=4, part=(None, B_)) == INVALID
+    # an empty batch is a valid no-op
+    assert call(lib, dsv3(), batch=0) == OK
+    assert call(lib, dsv3(), batch=0, split=A, split_tokens=1024, total=0, part=(A, B_)) == OK
+
+
+def test_absorb_needs_weights_and_workspace(lib):
+    d = dsv3()
+    st = lib.gqla_decode_mqa_absorb(ctypes.byref(d), 1, A, A, A, A, 4, A, None, A, None, 0, 0, A,
+                                    None, None, None, A, 1 << 40, None)
+    assert st == INVALID
+    need = lib.gqla_mqa_absorb_workspace_bytes(ctypes.byref(d), 3)
+    assert need == 3 * 1 * 128 * 576 * 2
+    assert absorb(lib, d, batch=3, ws_bytes=need - 1) == INVALID
+    assert absorb(lib, d, batch=3, ws=None, ws_bytes=need) == INVALID
+    assert absorb(lib, d, batch=3, ws=ODD, ws_bytes=need) == MISALIGNED
+    assert lib.gqla_mqa_absorb_workspace_bytes(None, 3) == 0
+
+
+def test_expand_and_combine_argument_errors(lib):
+    d = dsv3()
+    assert lib.gqla_expand_cache(ctypes.byref(d), A, A, A, 10, None, 0, A, None) == OK   # nothing to do
+    assert lib.gqla_expand_cache(ctypes.byref(d), A, A, A, 10, None, 11, A, None) == INVALID
+    assert lib.gqla_expand_cache(ctypes.byref(d), ODD, A, A, 10, None, 10, A, None) == MISALIGNED
+    assert lib.gqla_expand_cache(ctypes.byref(d), None, A, A, 10, None, 10, A, None) == INVALID
+    assert lib.gqla_expand_cache(None, A, A, A, 10, None, 10, A, None) == INVALID
+    assert lib.gqla_splitkv_combine(ctypes.byref(d), 2, None, 4, A, A, A, None, None) == INVALID
+    assert lib.gqla_splitkv_combine(ctypes.byref(d), 2, A, 4, ODD, A, A, None, None) == MISALIGNED
+    assert lib.gqla_splitkv_combine(ctypes.byref(d), 0, A, 0, A, A, A, None, None) == OK
+    assert lib.gqla_splitkv_combine(ctypes.byref(d), -1, A, 0, A, A, A, None, None) == INVALID
+
+
+def test_binding_rejects_cpu_tensors_and_wrong_dtypes(lib):
+    d = Dims.make(16, 2, 64, 16, 32, 32, 1)
+    q = torch.zeros(1, 1, 16, 32, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        G.gqla_decode_gqa(d, q, q, q, torch.zeros(1, 1, dtype=torch.int32),
+                          torch.zeros(1, dtype=torch.int32), out=q)
+
+
+def test_split_plan_counts_ceil_per_sequence():
+    offs, total = G.make_split_plan([1, 1024, 1025, 4096], 1024, device="cpu")
+    assert offs.tolist() == [0, 1, 2, 4, 8] and total == 8
