@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""Decode throughput of GQLA attention on one MI355X, both paths.
+
+One step = one decode step of one DeepSeek-V3-shaped GQLA attention layer
+(128 query heads, 8 groups, latent 512 + rope 64, nope/v 128) over a batch of
+64 sequences at context 4096, on both decode paths of the same weights:
+  * MQA-absorb, s_q = 1, over the paged latent cache (1152 B/token), and
+  * GQA, s_q = 2 (one MTP row, causal between the two new tokens), over the
+    cache expanded once by gqla_expand_cache (4224 B/token).
+Tokens per step = 64 * 1 + 64 * 2.  Inputs are seeded synthetic tensors,
+resident in HBM before timing.  The one-shot expansion is timed separately
+and is not part of a step.
+
+Prints ONE JSON line (see the keys below).  `--gpus N` with N > 1 exits: this
+build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode tokens/s per MI355X, both paths, B=64 ctx 4K; % of roofline"
+WORKLOAD = ("DeepSeek-V3-shaped GQLA decode layer: 128 query heads, 8 groups, latent 512 + "
+            "rope 64, nope/v 128, batch 64, context 4096, paged cache (64-token pages); "
+            "MQA-absorb s_q=1 over the latent cache + GQA s_q=2 over the expanded cache")
+SRC_FILES = ["decode_attention_gqla_amd/csrc/gqa_decode.hip",
+             "decode_attention_gqla_amd/csrc/absorb_decode.hip",
+             "decode_attention_gqla_amd/csrc/common.hip.h",
+             "decode_attention_gqla_amd/csrc/combine.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in SRC_FILES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--absorb-split", type=int, default=1024,
+                    help="tokens per split-KV partition of the absorb path (0 = no split)")
+    ap.add_argument("--gqa-split", type=int, default=0,
+                    help="tokens per split-KV partition of the GQA path (0 = no split)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seqs", type=int, default=8,
+                    help="sequences of the batch the CPU oracle decodes (bounded sample)")
+    ap.add_argument("--only", choices=["absorb", "gqa"], default=None,
+                    help="profiling aid: run only one path per step (not a valid bench line)")
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="run only a plain device copy of this many bytes (counter calibration)")
+    return ap.parse_args()
+
+
+def copy_probe(nbytes: int):
+    import torch
+    n = nbytes // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n * 4, "dispatches": 3}))
+
+
+def cpu_baseline(case_abs, case_gqa, n_seqs: int):
+    """fp64 CPU oracle on a bounded sample: the literal decode of the first
+    n_seqs sequences on both paths' row sets."""
+    import numpy as np
+    from oracle.gqla_ref import Dims, decode_literal
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    f = lambda t: t.double().numpy()
+    seqs = list(range(n_seqs))
+    t0 = time.perf_counter()
+    toks = 0
+    for case in (case_abs, case_gqa):
+        d = Dims(h_q=case.h_q, g=case.g, r=case.r, d_R=case.d_R, d_nope=case.d_nope,
+                 d_v=case.d_v, s_q=case.s_q, bs=case.bs)
+        decode_literal(f(case.q_nope), f(case.q_rope), f(case.pages), case.block_table.numpy(),
+                       case.seqlens.numpy(), f(case.w_uk), f(case.w_uv), d, seqs=seqs)
+        toks += n_seqs * case.s_q
+    dt = time.perf_counter() - t0
+    return {"value": toks / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"fp64 numpy literal decode (expand per group, then softmax attention) of "
+                      f"{n_seqs} of the 64 sequences on both paths ({toks} tokens, {dt:.1f} s)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the GQA path would shard by KV group across GPUs, see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
+    import decode_attention_gqla_amd as G
+    from decode_attention_gqla_amd import roofline as rf
+    from decode_attention_gqla_amd.inputs import config_case
+
+    G.lib()
+    log("generating inputs")
+    case_abs = config_case("dsv3", 1)
+    case_gqa = config_case("dsv3", 2, seed=1002 + 10)      # same weights and cache (same seed)
+    assert torch.equal(case_abs.pages, case_gqa.pages) and torch.equal(case_abs.w_uv, case_gqa.w_uv)
+    dev = "cuda"
+    d1, d2 = G.Dims.of(case_abs), G.Dims.of(case_gqa)
+    pages = case_abs.pages.to(dev)
+    bt = case_abs.block_table.to(dev)
+    sl = case_abs.seqlens.to(dev)
+    w_uk, w_uv = case_abs.w_uk.to(dev), case_abs.w_uv.to(dev)
+    qa_n, qa_r = case_abs.q_nope.to(dev), case_abs.q_rope.to(dev)
+    qg_n, qg_r = case_gqa.q_nope.to(dev), case_gqa.q_rope.to(dev)
+    B = case_abs.batch
+    lens = [int(x) for x in case_abs.seqlens]
+
+    # one-shot expansion (timed separately; not part of a step)
+    E = G.expand_cache(d2, pages, w_uk, w_uv)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    G.gqla_expand_cache(d2, pages, w_uk, w_uv, E)
+    ev1.record()
+    torch.cuda.synchronize()
+    t_expand_us = ev0.elapsed_time(ev1) * 1e3
+
+    out_a = torch.empty(B, 1, 128, 128, dtype=torch.bfloat16, device=dev)
+    lse_a = torch.empty(B, 1, 128, dtype=torch.float32, device=dev)
+    out_g = torch.empty(B, 2, 128, 128, dtype=torch.bfloat16, device=dev)
+    lse_g = torch.empty(B, 2, 128, dtype=torch.float32, device=dev)
+    ws = G.absorb_workspace(d1, B)
+    sa = G.make_split_plan(lens, args.absorb_split) + (args.absorb_split,) if args.absorb_split else None
+    sg = G.make_split_plan(lens, args.gqa_split) + (args.gqa_split,) if args.gqa_split else None
+    pa = (torch.empty(sa[1], 1, 128, 128, dtype=torch.float32, device=dev),
+          torch.empty(sa[1], 1, 128, dtype=torch.float32, device=dev)) if sa else (None, None)
+    pg = (torch.empty(sg[1], 2, 128, 128, dtype=torch.float32, device=dev),
+          torch.empty(sg[1], 2, 128, dtype=torch.float32, device=dev)) if sg else (None, None)
+
+    def run_absorb():
+        G.gqla_decode_mqa_absorb(d1, qa_n, qa_r, pages, bt, sl, w_uk, w_uv, out=out_a, lse=lse_a,
+                                 split_offsets=sa[0] if sa else None,
+                                 split_tokens=sa[2] if sa else 0, total_splits=sa[1] if sa else 0,
+                                 part_out=pa[0], part_lse=pa[1], workspace=ws)
+
+    def run_gqa():
+        G.gqla_decode_gqa(d2, qg_n, qg_r, E, bt, sl, out=out_g, lse=lse_g,
+                          split_offsets=sg[0] if sg else None, split_tokens=sg[2] if sg else 0,
+                          total_splits=sg[1] if sg else 0, part_out=pg[0], part_lse=pg[1])
+
+    paths = [("mqa_absorb", run_absorb), ("gqa", run_gqa)]
+    if args.only:
+        paths = [p for p in paths if p[0] == {"absorb": "mqa_absorb", "gqa": "gqa"}[args.only]]
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        for _, fn in paths:
+            fn()
+    torch.cuda.synchronize()
+    # timed region: K steps; per-path events on the launch stream
+    evs = {name: [] for name, _ in paths}
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for _ in range(args.steps):
+        for name, fn in paths:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            evs[name].append((a, b))
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    per_path = {}
+    for name, _ in paths:
+        us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs[name])
+        per_path[name] = {"us_mean": sum(us) / len(us), "us_median": us[len(us) // 2],
+                          "us_p10": us[len(us) // 10], "us_p90": us[(9 * len(us)) // 10]}
+    w_abs = rf.work_absorb(lens, 128, 8, 512, 64, 128, 128, 1)
+    w_gqa = rf.work_gqa(lens, 128, 8, 64, 128, 128, 2)
+    works = {"mqa_absorb": (w_abs, B * 1), "gqa": (w_gqa, B * 2)}
+    tokens = sum(works[n][1] for n, _ in paths)
+    for name, _ in paths:
+        w, tk = works[name]
+        t = per_path[name]["us_mean"]
+        per_path[name].update({
+            "tokens": tk, "tok_s": tk / (t * 1e-6),
+            "alg_bytes": w.bytes, "alg_flops": w.flops, "bound": w.bound(),
+            "achieved_GBps": w.bytes / (t * 1e-6) / 1e9,
+            "achieved_TFLOPs": w.flops / (t * 1e-6) / 1e12,
+            "roofline_us": w.roofline_us(), "roofline_frac": w.roofline_us() / t,
+        })
+    dom = max(per_path, key=lambda n: per_path[n]["us_mean"])
+    wd = works[dom][0]
+    td = per_path[dom]["us_mean"]
+    traffic = None
+    src_hash = kernel_source_hash()
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            tr = json.load(open(TRAFFIC_FILE))
+            ent = tr.get(dom)
+            if ent and ent.get("source_hash") == src_hash:
+                traffic = ent.get("bytes_per_launch")
+        except Exception:  # pragma: no cover
+            traffic = None
+    if wd.bound() == "hbm":
+        roof = {"bound": "hbm", "achieved": wd.bytes / (td * 1e-6) / 1e9, "peak": rf.MI355X_HBM_GBPS,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": wd.flops / (td * 1e-6) / 1e12,
+                "peak": rf.MI355X_BF16_TFLOPS, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic
+    roof["kernel"] = dom
+    cpu = None
+    if not args.no_cpu and not args.only:
+        log("cpu oracle baseline")
+        cpu = cpu_baseline(case_abs, case_gqa, args.cpu_seqs)
+    line = {
+        "metric": METRIC,
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": WORKLOAD, "global_batch": B, "seq_len": 4096,
+                   "absorb_split_tokens": args.absorb_split, "gqa_split_tokens": args.gqa_split,
+                   "only": args.only},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "paths": per_path,
+        "expand_us": t_expand_us,
+        "kernel_source_hash": src_hash,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -76,6 +76,44 @@ __device__ __forceinline__ float wave_sum_xor16_32(float v) {
   return v;
 }
 
+typedef __attribute__((address_space(3))) unsigned char lds_u8_t;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4_t;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+
+// Direct HBM -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane
+// i reads base + voff_bytes(i) and its 16 bytes land at lds_base + 16 * i.
+// `base` and `lds_base` must be wave-uniform.  Issued from inline asm so that
+// the compiler does not add its own conservative waits for it (it cannot tell
+// which LDS buffer a copy targets and would wait for every copy in flight);
+// callers wait with vm_wait<N>() before reading the buffer.  M0 is written in
+// the same asm block; the one wait state between the M0 write and the copy is
+// the s_nop.  There are no register outputs.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff_bytes, lds_u8_t* lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff_bytes), "s"(base), "s"((uint32_t)(uintptr_t)lds_base) : "memory", "m0");
+}
+
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
+// [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at their maxima),
+// followed by a compiler barrier so LDS reads are not hoisted above it.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+
+// Scalar load of one wave-uniform int32 (e.g. a block-table entry).  Done in
+// asm with its wait in the same block: a vector load here would make the wave
+// wait on every vector-memory operation in flight (the in-order vmcnt),
+// including the tile prefetches, while the scalar path only uses lgkmcnt.
+// `ptr` must be wave-uniform and 4-byte aligned.
+__device__ __forceinline__ int sload_i32(const int32_t* ptr) {
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
+  return v;
+}
+
 // Find the sequence owning split w: largest b with split_offsets[b] <= w.
 __device__ __forceinline__ int split_owner(const int32_t* __restrict__ offs, int batch, int w) {
   int lo = 0, hi = batch - 1;

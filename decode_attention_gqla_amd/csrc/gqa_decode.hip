@@ -7,66 +7,65 @@
 //
 // Work decomposition: one wave (one 64-lane workgroup) per (split unit, group).
 // The wave's query rows (h_q/g heads x s_q tokens, padded to 16-row tiles)
-// stay in registers; the wave streams its group's K block, dim-major V block
-// and the shared rope key straight from HBM into MFMA operand registers, two
-// 32-token tiles in flight, so nothing is staged through LDS.
-//
+// stay in registers.  Each 32-token tile of the group's K block, dim-major V
+// block and the shared rope key is copied HBM -> LDS by direct DMA
+// (global_load_lds_dwordx4, three tiles in flight per wave, no VGPR staging),
+// then read as bf16 MFMA operands (the copies are waited for explicitly with
+// vmcnt, see dma16):
 //   S^T[token][row] = K[token][:] . Q[row][:]        (A = cache rows, B = Q^T)
 //   O^T[dim][row]  += V^T[dim][token] . P^T[token][row]
-// The token order inside a 32-token tile is relabelled so that the S^T
-// accumulator lane layout is exactly the P^T B-operand layout of the PV
-// product (lane group q holds tokens 8q..8q+7), and V^T is stored dim-major
-// so its A operand is one contiguous 16-byte load per lane.
+// The token order inside a tile is relabelled so that the S^T accumulator lane
+// layout is exactly the P^T B-operand layout of the PV product (lane group q
+// holds tokens 8q..8q+7), and V^T is stored dim-major, so no operand needs a
+// transpose.  The LDS copies are XOR-swizzled in 16-byte chunks so every
+// operand read is bank-conflict free.
 #include "common.hip.h"
 #include "params.hip.h"
 
 namespace gqla {
 
+
 template <int HPG, int SQ, int DN, int DV, int DR>
 struct GqaCfg {
   static constexpr int BS = 64;
+  static constexpr int TILE = 32;
+  static constexpr int NBUF = 3;
   static constexpr int ROWS = HPG * SQ;
   static constexpr int NT = (ROWS + 15) / 16;     // 16-row tiles
   static constexpr int KSN = DN / 32;             // 32-wide k steps over d_nope
   static constexpr int KSR = (DR + 31) / 32;      // over d_rope (zero padded)
   static constexpr int MT = DV / 16;              // 16-dim output tiles
-  static_assert(DN % 32 == 0 && DV % 16 == 0, "unsupported head dims");
+  static constexpr int KCH = DN / 8;              // 16-byte chunks per K row
+  static constexpr int RCH = DR / 8;              // 16-byte chunks per rope row
+  static constexpr int VCH = TILE / 8;            // 16-byte chunks per V^T row (4)
+  static constexpr int K_BYTES = TILE * DN * 2;
+  static constexpr int V_BYTES = DV * TILE * 2;
+  static constexpr int R_BYTES = TILE * DR * 2;
+  static constexpr int TILE_BYTES = K_BYTES + V_BYTES + R_BYTES;
+  static constexpr int NI_K = K_BYTES / 1024, NI_V = V_BYTES / 1024;
+  static constexpr int NI_R = (R_BYTES + 1023) / 1024;
+  static constexpr int NI = NI_K + NI_V + NI_R;   // DMA instructions per tile
+  static_assert(DN % 32 == 0 && DV % 16 == 0 && DR % 8 == 0, "unsupported head dims");
+  static_assert(K_BYTES % 1024 == 0 && V_BYTES % 1024 == 0, "whole DMA instructions");
+  static_assert(2 * NI < 64, "vmcnt budget");
+  static_assert((KCH & (KCH - 1)) == 0 && (RCH & (RCH - 1)) == 0, "power-of-two rows");
 };
 
-template <class C>
-struct GqaTile {
-  bf16x8 k[2][C::KSN];
-  bf16x8 r[2][C::KSR];
-  bf16x8 v[C::MT];
-};
-
-template <class C, int DN, int DV, int DR>
-__device__ __forceinline__ void gqa_load_tile(GqaTile<C>& T, const uint16_t* __restrict__ page,
-                                              int G, int g, int slot0, int lane) {
-  constexpr int BS = C::BS;
-  const int c = lane & 15, q = lane >> 4;
-  const uint16_t* kblk = page + (size_t)G * BS * (DN + DV);
-  const uint16_t* vblk = kblk + BS * DN;
-  const uint16_t* rope = page + (size_t)g * BS * (DN + DV);
-#pragma unroll
-  for (int st = 0; st < 2; ++st) {
-    const int slot = slot0 + 8 * (c >> 2) + 4 * st + (c & 3);
-#pragma unroll
-    for (int ks = 0; ks < C::KSN; ++ks) T.k[st][ks] = ld_bf16x8(kblk + slot * DN + 32 * ks + 8 * q);
-#pragma unroll
-    for (int ks = 0; ks < C::KSR; ++ks) {
-      const int dim = 32 * ks + 8 * q;
-      T.r[st][ks] = (dim < DR) ? ld_bf16x8(rope + slot * DR + dim) : zero_bf16x8();
-    }
-  }
-#pragma unroll
-  for (int mt = 0; mt < C::MT; ++mt) T.v[mt] = ld_bf16x8(vblk + (16 * mt + c) * BS + slot0 + 8 * q);
-}
+// Token swizzles (tile-local token t in 0..31).  The QK reads touch 16 tokens
+// {8a + 4st + b} (a, b in 0..3) at one chunk: kswz is distinct over them.
+__device__ __forceinline__ int kswz(int t) { return (t & 3) | ((t >> 3) << 2); }
+__device__ __forceinline__ int rswz(int t) { return ((t >> 1) & 1) | ((t >> 3) << 1); }
+// V^T rows d: 16 consecutive rows, one chunk -> distinct (d%4, chunk) bank groups.
+__device__ __forceinline__ int vswz(int d) { return (d >> 2) & 3; }
 
 template <int HPG, int SQ, int DN, int DV, int DR>
 __global__ __launch_bounds__(64) void gqa_decode_kernel(DecodeParams p) {
   using C = GqaCfg<HPG, SQ, DN, DV, DR>;
   constexpr int BS = C::BS, NT = C::NT, KSN = C::KSN, KSR = C::KSR, MT = C::MT;
+  constexpr int KCH = C::KCH, RCH = C::RCH, VCH = C::VCH;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[C::NBUF * C::TILE_BYTES];
+  lds_u8_t* const lds = (lds_u8_t*)lds_raw;
+
   const int g = p.num_groups;
   const int H = HPG * g;
   // Workgroups are dispatched round-robin over the 8 XCDs; give the g groups
@@ -83,9 +82,8 @@ __global__ __launch_bounds__(64) void gqa_decode_kernel(DecodeParams p) {
   if (p.split_offsets) {
     b = split_owner(p.split_offsets, p.batch, u);
     const int j = u - p.split_offsets[b];
-    const int L = p.seqlens[b];
     lo = j * p.split_tokens;
-    hi = min(lo + p.split_tokens, L);
+    hi = min(lo + p.split_tokens, p.seqlens[b]);
   } else {
     b = u;
     lo = 0;
@@ -94,6 +92,39 @@ __global__ __launch_bounds__(64) void gqa_decode_kernel(DecodeParams p) {
   const int L = p.seqlens[b];
   const int c = lane & 15, q = lane >> 4;
   const size_t page_elems = (size_t)BS * (g * (DN + DV) + DR);
+  const int n_tiles = hi > lo ? (hi - lo + C::TILE - 1) / C::TILE : 0;
+  const int32_t* bt = p.block_table + (size_t)b * p.max_blocks;     // wave-uniform
+
+  // ---- DMA of tile `it` into `dst` (the buffer of tile it % 3) ----
+  auto issue_tile = [&](int it) {
+    lds_u8_t* dst = lds + (it % C::NBUF) * C::TILE_BYTES;
+    const int t0 = lo + C::TILE * it;
+    const uint16_t* page = p.cache + (size_t)sload_i32(bt + t0 / BS) * page_elems;
+    const int slot0 = t0 % BS;
+    const uint16_t* kblk = page + (size_t)G * BS * (DN + DV) + slot0 * DN;
+    const uint16_t* vblk = page + (size_t)G * BS * (DN + DV) + BS * DN + slot0;
+    const uint16_t* rope = page + (size_t)g * BS * (DN + DV) + slot0 * DR;
+#pragma unroll
+    for (int i = 0; i < C::NI_K; ++i) {        // K rows: token-major, chunk swizzled
+      const int P = i * 64 + lane, t = P / KCH, pos = P % KCH;
+      const int ch = pos ^ (kswz(t) & (KCH - 1));
+      dma16(kblk, (uint32_t)(t * DN + ch * 8) * 2u, dst + i * 1024);
+    }
+#pragma unroll
+    for (int i = 0; i < C::NI_V; ++i) {        // V^T rows: 32 tokens of one dim
+      const int P = i * 64 + lane, d = P / VCH, pos = P % VCH;
+      const int ch = pos ^ vswz(d);
+      dma16(vblk, (uint32_t)(d * BS + ch * 8) * 2u, dst + C::K_BYTES + i * 1024);
+    }
+#pragma unroll
+    for (int i = 0; i < C::NI_R; ++i) {        // rope rows: token-major, chunk swizzled
+      int P = i * 64 + lane;
+      if (P >= C::TILE * RCH) P = C::TILE * RCH - 1;   // partial last instruction: duplicate
+      const int t = P / RCH, pos = P % RCH;
+      const int ch = pos ^ (rswz(t) & (RCH - 1));
+      dma16(rope, (uint32_t)(t * DR + ch * 8) * 2u, dst + C::K_BYTES + C::V_BYTES + i * 1024);
+    }
+  };
 
   // Query rows of this group as B operands (Q^T): lane (q, c) holds 8 dims of row c.
   bf16x8 qb[NT][KSN + KSR];
@@ -114,6 +145,12 @@ __global__ __launch_bounds__(64) void gqa_decode_kernel(DecodeParams p) {
     }
   }
 
+  // The query loads complete before the first tile copy is issued, so the
+  // compiler's own wait tracking has nothing pending inside the tile loop.
+  vm_wait<0>();
+  if (n_tiles > 0) issue_tile(0);
+  if (n_tiles > 1) issue_tile(1);
+
   f32x4 o[MT][NT];
   float m_run[NT], l_run[NT];
   int nvis[NT];
@@ -127,29 +164,44 @@ __global__ __launch_bounds__(64) void gqa_decode_kernel(DecodeParams p) {
     nvis[nt] = L - SQ + (rho < C::ROWS ? rho % SQ : SQ - 1) + 1;
   }
 
-  const int32_t* bt = p.block_table + (size_t)b * p.max_blocks;
-  auto page_of = [&](int t0) -> const uint16_t* {
-    return p.cache + (size_t)bt[t0 / BS] * page_elems;
-  };
+  for (int it = 0; it < n_tiles; ++it) {
+    // prefetch tile it+2 into the buffer of tile it-1 (already consumed), then
+    // wait until tile it has landed
+    if (it + 2 < n_tiles) {
+      issue_tile(it + 2);
+      vm_wait<2 * C::NI>();
+    } else if (it + 1 < n_tiles) {
+      vm_wait<C::NI>();
+    } else {
+      vm_wait<0>();
+    }
+    const lds_u8_t* buf = lds + (it % C::NBUF) * C::TILE_BYTES;
+    const int t0 = lo + C::TILE * it;
 
-  auto compute = [&](GqaTile<C>& T, int t0) {
     f32x4 s[2][NT];
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+    for (int st = 0; st < 2; ++st) {
+      const int t = 8 * (c >> 2) + 4 * st + (c & 3);     // token held by MFMA row c
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int nt = 0; nt < NT; ++nt) s[st][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KSN; ++ks) acc = mfma16(T.k[st][ks], qb[nt][ks], acc);
+      for (int ks = 0; ks < KSN; ++ks) {
+        const int pos = (4 * ks + q) ^ (kswz(t) & (KCH - 1));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, *(const lds_u32x4_t*)(buf + (t * KCH + pos) * 16));
 #pragma unroll
-        for (int ks = 0; ks < KSR; ++ks) acc = mfma16(T.r[st][ks], qb[nt][KSN + ks], acc);
-        s[st][nt] = acc;
+        for (int nt = 0; nt < NT; ++nt) s[st][nt] = mfma16(a, qb[nt][ks], s[st][nt]);
       }
-    // tokens past the end of the sequence may hold anything: keep their V at 0
-    if (t0 + 32 > L) {
-      const int keep = min(max(L - (t0 + 8 * q), 0), 8);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) T.v[mt] = keep_first(T.v[mt], keep);
+      for (int ks = 0; ks < KSR; ++ks) {
+        const int ch = 4 * ks + q;
+        bf16x8 a = zero_bf16x8();
+        if (8 * ch < DR) {
+          const int pos = ch ^ (rswz(t) & (RCH - 1));
+          a = __builtin_bit_cast(bf16x8, *(const lds_u32x4_t*)(buf + C::K_BYTES + C::V_BYTES + (t * RCH + pos) * 16));
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) s[st][nt] = mfma16(a, qb[nt][KSN + ks], s[st][nt]);
+      }
     }
     bf16x8 pb[NT];
 #pragma unroll
@@ -183,22 +235,17 @@ __global__ __launch_bounds__(64) void gqa_decode_kernel(DecodeParams p) {
                   pack_bf16x2(x[6], x[7])};
       pb[nt] = __builtin_bit_cast(bf16x8, pk);
     }
+    // tokens past the end of the sequence may hold anything: keep their V at 0
+    const bool tail = t0 + C::TILE > L;
+    const int keep = min(max(L - (t0 + 8 * q), 0), 8);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int mt = 0; mt < MT; ++mt) {
+      const int d = 16 * mt + c;
+      const int pos = q ^ vswz(d);
+      bf16x8 v = __builtin_bit_cast(bf16x8, *(const lds_u32x4_t*)(buf + C::K_BYTES + (d * VCH + pos) * 16));
+      if (tail) v = keep_first(v, keep);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) o[mt][nt] = mfma16(T.v[mt], pb[nt], o[mt][nt]);
-  };
-
-  const int n_tiles = (hi - lo + 31) / 32;
-  GqaTile<C> ta, tb;
-  if (n_tiles > 0) gqa_load_tile<C, DN, DV, DR>(ta, page_of(lo), G, g, lo % BS, lane);
-  for (int it = 0; it < n_tiles; it += 2) {
-    const int t0 = lo + 32 * it;
-    if (it + 1 < n_tiles) gqa_load_tile<C, DN, DV, DR>(tb, page_of(t0 + 32), G, g, (t0 + 32) % BS, lane);
-    compute(ta, t0);
-    if (it + 1 < n_tiles) {
-      if (it + 2 < n_tiles) gqa_load_tile<C, DN, DV, DR>(ta, page_of(t0 + 64), G, g, (t0 + 64) % BS, lane);
-      compute(tb, t0 + 32);
+      for (int nt = 0; nt < NT; ++nt) o[mt][nt] = mfma16(v, pb[nt], o[mt][nt]);
     }
   }
 
@@ -216,7 +263,7 @@ __global__ __launch_bounds__(64) void gqa_decode_kernel(DecodeParams p) {
       const size_t row = ((size_t)u * SQ + iq) * H + h;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        f32x4 v = o[mt][nt] * inv;
+        const f32x4 v = o[mt][nt] * inv;
         *reinterpret_cast<f32x4*>(p.part_out + row * DV + 16 * mt + 4 * q) = v;
       }
       if (q == 0) p.part_lse[row] = lse_v;

@@ -102,6 +102,7 @@ gqla::DecodeParams make_params(const gqla_dims* d, int32_t batch, const void* q_
   p.num_units = split_offsets ? total_splits : batch;
   p.scale_log2 = scale_of(d) * gqla::kLog2e;
   p.qcat = nullptr;
+  p.wuvT = nullptr;
   return p;
 }
 
@@ -154,10 +155,18 @@ int64_t gqla_expanded_page_elems(const gqla_dims* d) {
   return (int64_t)d->block_size * ((int64_t)d->num_groups * (d->d_nope + d->d_v) + d->d_rope);
 }
 
+// Workspace of the absorb path: the absorbed queries [batch][s_q][h_q][r + d_rope]
+// (bf16), then (256-byte aligned) W_UV transposed, [g][d_v][r] (bf16).
+static uint64_t absorb_q_bytes(const gqla_dims* d, int32_t batch) {
+  const uint64_t n = (uint64_t)batch * d->s_q * d->num_heads * (uint64_t)(d->d_latent + d->d_rope) * 2u;
+  return (n + 255u) & ~(uint64_t)255u;
+}
+
 uint64_t gqla_mqa_absorb_workspace_bytes(const gqla_dims* d, int32_t batch) {
-  if (!d || batch <= 0 || d->s_q <= 0 || d->num_heads <= 0 || d->d_latent <= 0 || d->d_rope < 0)
+  if (!d || batch <= 0 || d->s_q <= 0 || d->num_heads <= 0 || d->d_latent <= 0 || d->d_rope < 0 ||
+      d->num_groups <= 0 || d->d_v <= 0)
     return 0;
-  return (uint64_t)batch * d->s_q * d->num_heads * (uint64_t)(d->d_latent + d->d_rope) * 2u;
+  return absorb_q_bytes(d, batch) + (uint64_t)d->num_groups * d->d_v * (uint64_t)d->d_latent * 2u;
 }
 
 int gqla_expand_cache(const gqla_dims* d, const void* latent_pages, const void* w_uk,
@@ -208,6 +217,7 @@ int gqla_decode_mqa_absorb(const gqla_dims* d, int32_t batch, const void* q_nope
                                      max_blocks, cache_seqlens, w_uk, w_uv, split_offsets,
                                      split_tokens, total_splits, out, lse, part_out, part_lse);
   p.qcat = (uint16_t*)workspace;
+  p.wuvT = (uint16_t*)((char*)workspace + absorb_q_bytes(d, batch));
   bool ok = true;
   hipError_t e = gqla::absorb_dispatch(d->num_heads / d->num_groups, d->s_q, d->d_latent,
                                        d->d_nope, d->d_v, d->d_rope, p, (hipStream_t)stream, &ok);

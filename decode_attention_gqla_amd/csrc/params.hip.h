@@ -14,6 +14,7 @@ struct DecodeParams {
   const uint16_t* w_uv;          // [g][r][d_v]      (absorb path only)
   const int32_t* split_offsets;  // [B+1] or nullptr
   uint16_t* qcat;                // absorb path: [B][s_q][h_q][r + d_rope] workspace
+  uint16_t* wuvT;                // absorb path: [g][d_v][r] workspace (W_UV transposed)
   uint16_t* out;                 // [B][s_q][h_q][d_v] bf16 (unsplit launch)
   float* lse;                    // [B][s_q][h_q] or nullptr (unsplit launch)
   float* part_out;               // [S][s_q][h_q][d_v] (split launch)

@@ -132,9 +132,9 @@ int gqla_expand_cache(const gqla_dims* d, const void* latent_pages, const void* 
  *            (exact by linearity), so partials are in the output space.
  *   workspace  device scratch of at least gqla_mqa_absorb_workspace_bytes(d, batch)
  *            bytes, 16-byte aligned, owned by the caller; it receives the
- *            absorbed queries [batch][s_q][h_q][d_latent + d_rope] (bf16) and must
- *            not be shared by calls that may run concurrently.  Too small or NULL
- *            returns GQLA_ERR_INVALID_ARG. */
+ *            absorbed queries [batch][s_q][h_q][d_latent + d_rope] (bf16) and a
+ *            transposed copy of W_UV, and must not be shared by calls that may
+ *            run concurrently.  Too small or NULL returns GQLA_ERR_INVALID_ARG. */
 int gqla_decode_mqa_absorb(const gqla_dims* d, int32_t batch, const void* q_nope,
                            const void* q_rope, const void* latent_pages,
                            const int32_t* block_table, int32_t max_blocks,

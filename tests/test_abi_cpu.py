@@ -110,7 +110,7 @@ def test_absorb_needs_weights_and_workspace(lib):
                                     None, None, None, A, 1 << 40, None)
     assert st == INVALID
     need = lib.gqla_mqa_absorb_workspace_bytes(ctypes.byref(d), 3)
-    assert need == 3 * 1 * 128 * 576 * 2
+    assert need == 3 * 1 * 128 * 576 * 2 + 8 * 128 * 512 * 2
     assert absorb(lib, d, batch=3, ws_bytes=need - 1) == INVALID
     assert absorb(lib, d, batch=3, ws=None, ws_bytes=need) == INVALID
     assert absorb(lib, d, batch=3, ws=ODD, ws_bytes=need) == MISALIGNED
