@@ -59,7 +59,7 @@ def parse():
     ap.add_argument("--gqa-split", type=int, default=0,
                     help="tokens per split-KV partition of the GQA path (0 = no split)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seqs", type=int, default=8,
+    ap.add_argument("--cpu-seqs", type=int, default=64,
                     help="sequences of the batch the CPU oracle decodes (bounded sample)")
     ap.add_argument("--only", choices=["absorb", "gqa"], default=None,
                     help="profiling aid: run only one path per step (not a valid bench line)")

@@ -234,17 +234,19 @@ __global__ __launch_bounds__(512, 1) void absorb_decode_kernel(DecodeParams p) {
         const int off = qk_base(z, st, C::SWZ ? (ks & 1) : 0) + 64 * ks;
         return __builtin_bit_cast(bf16x8, *(const lds_u32x4_t*)(buf + off));
       };
-      // one token subtile at a time, operands read one step ahead; the
+      // one token subtile at a time, operands read three steps ahead; the
       // compiler barrier per step keeps the remaining reads from being hoisted
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         f32x4 s0 = {0.f, 0.f, 0.f, 0.f};
-        bf16x8 a0 = qk_operand(st, 0), a1 = zero_bf16x8();
+        constexpr int PD = 3;
+        bf16x8 a[PD + 1];
+#pragma unroll
+        for (int j = 0; j < PD && j < KSH; ++j) a[j] = qk_operand(st, j);
 #pragma unroll
         for (int j = 0; j < KSH; ++j) {
-          if (j + 1 < KSH) a1 = qk_operand(st, j + 1);
-          s0 = mfma16(a0, qb[j], s0);
-          a0 = a1;
+          if (j + PD < KSH) a[(j + PD) % (PD + 1)] = qk_operand(st, j + PD);
+          s0 = mfma16(a[j % (PD + 1)], qb[j], s0);
           asm volatile("" ::: "memory");
         }
         *(__attribute__((address_space(3))) f32x4*)(sp + (((kh * NTW + rt) * 2 + st) * 64 + lane) * 16) = s0;
@@ -256,6 +258,8 @@ __global__ __launch_bounds__(512, 1) void absorb_decode_kernel(DecodeParams p) {
 
     // ---- softmax for rows 16w .. 16w+15 (waves 0 .. NTW-1) ----
     if (smax_wave) {
+      // masking is needed only on tiles that reach the first causal bound
+      const bool masked = t0 + C::TILE > L - SQ + 1 || !svalid;
       float x[8];
       float mx = -INFINITY;
 #pragma unroll
@@ -265,10 +269,10 @@ __global__ __launch_bounds__(512, 1) void absorb_decode_kernel(DecodeParams p) {
         const f32x4 a1 = *(const __attribute__((address_space(3))) f32x4*)(sp + (base + NTW * 2 * 64) * 16);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int tok = t0 + 8 * q + 4 * st + i;
-          const float v = (a0[i] + a1[i]) * p.scale_log2;
-          x[4 * st + i] = (tok < s_nvis) ? v : -INFINITY;
-          mx = fmaxf(mx, x[4 * st + i]);
+          float v = (a0[i] + a1[i]) * p.scale_log2;
+          if (masked) v = (t0 + 8 * q + 4 * st + i < s_nvis) ? v : -INFINITY;
+          x[4 * st + i] = v;
+          mx = fmaxf(mx, v);
         }
       }
       mx = wave_max_xor16_32(mx);
@@ -277,7 +281,7 @@ __global__ __launch_bounds__(512, 1) void absorb_decode_kernel(DecodeParams p) {
       const bool resc = __any(mx > m_run + 8.f);
       if (resc) {
         const float m_new = fmaxf(m_run, mx);
-        const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
+        const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
         m_run = m_new;
         if (q == 0) al[srow] = alpha;
@@ -287,7 +291,7 @@ __global__ __launch_bounds__(512, 1) void absorb_decode_kernel(DecodeParams p) {
       float ps = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        x[j] = exp2f(x[j] - m_use);
+        x[j] = __builtin_amdgcn_exp2f(x[j] - m_use);
         ps += x[j];
       }
       l_run += ps;
@@ -299,9 +303,16 @@ __global__ __launch_bounds__(512, 1) void absorb_decode_kernel(DecodeParams p) {
 
     // ---- PV for latent tiles mt0 .. mt0+MTW-1 of all the block's rows ----
     if (pv_active) {
+      int flags[NTW];
+#pragma unroll
+      for (int nt = 0; nt < NTW; nt += 4) {
+        const u32x4 f4 = *(const lds_u32x4_t*)(lds + C::OFF_FL + nt * 4);
+#pragma unroll
+        for (int k2 = 0; k2 < 4 && nt + k2 < NTW; ++k2) flags[nt + k2] = (int)f4[k2];
+      }
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) {
-        if (fl[nt]) {                             // rows of n-tile nt moved their reference
+        if (flags[nt]) {                          // rows of n-tile nt moved their reference
           const float a = al[16 * nt + c];
 #pragma unroll
           for (int j = 0; j < MTW; ++j) o[j][nt] *= a;
@@ -433,6 +444,7 @@ __global__ __launch_bounds__(512, 1) void absorb_decode_kernel(DecodeParams p) {
 template <int HPG, int SQ, int R, int DR, int DN>
 __global__ __launch_bounds__(256) void absorb_q_kernel(DecodeParams p) {
   constexpr int ROW = R + DR, KD = DN / 32, MT = R / 16;
+  constexpr int MTC = MT < 8 ? MT : 8;               // latent tiles per workgroup (blockIdx.z)
   const int g = p.num_groups, H = HPG * g;
   const int rows_g = p.batch * SQ * HPG;             // query rows of one group
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -451,8 +463,9 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(DecodeParams p) {
     qn[kd] = valid ? ld_bf16x8(p.q_nope + qrow * DN + 32 * kd + 8 * q) : zero_bf16x8();
   const uint16_t* W = p.w_uk + (size_t)G * R * DN;
   uint16_t* dst = p.qcat + qrow * ROW;
-#pragma unroll 4
-  for (int mt = 0; mt < MT; ++mt) {
+  const int mt0 = blockIdx.z * MTC;
+#pragma unroll
+  for (int mt = mt0; mt < mt0 + MTC; ++mt) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kd = 0; kd < KD; ++kd)
@@ -464,6 +477,7 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(DecodeParams p) {
     }
   }
   // rope part copied unchanged
+  if (blockIdx.z != 0) return;
   for (int id = lane; id < 16 * DR / 8; id += 64) {
     const int rr = id / (DR / 8), part = id % (DR / 8);
     const int gr2 = r0 + rr;
@@ -495,7 +509,8 @@ hipError_t launch_absorb(const DecodeParams& p, hipStream_t stream) {
   using C = AbsorbCfg<HPG, SQ, R, DR, DN, DV>;
   {
     const int rows_g = p.batch * SQ * HPG;
-    dim3 grid((unsigned)((rows_g + 63) / 64), (unsigned)p.num_groups);
+    constexpr int MT = R / 16, MTC = MT < 8 ? MT : 8;
+    dim3 grid((unsigned)((rows_g + 63) / 64), (unsigned)p.num_groups, (unsigned)(MT / MTC));
     hipLaunchKernelGGL((absorb_q_kernel<HPG, SQ, R, DR, DN>), grid, dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

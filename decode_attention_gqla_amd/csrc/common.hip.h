@@ -35,8 +35,12 @@ __device__ __forceinline__ uint16_t f2bf_bits(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Two fp32 -> packed bf16 (lo in bits 0..15), round to nearest even, by the
+// hardware conversion (v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f2bf_bits(lo) | ((uint32_t)f2bf_bits(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 __device__ __forceinline__ float bf_bits2f(uint32_t bits16) {

@@ -203,36 +203,54 @@ __global__ __launch_bounds__(64) void gqa_decode_kernel(DecodeParams p) {
         for (int nt = 0; nt < NT; ++nt) s[st][nt] = mfma16(a, qb[nt][KSN + ks], s[st][nt]);
       }
     }
-    bf16x8 pb[NT];
+    // Online softmax (base 2).  Masking is needed only on tiles that reach
+    // the first causal bound (L - s_q + 1); the reference max moves lazily:
+    // the accumulators are rescaled only when some row's max exceeds its
+    // reference by more than 8 (so every p <= 2^8), which is rare after the
+    // first tile.
+    const bool masked = t0 + C::TILE > L - SQ + 1;
+    float x[NT][8], mx[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      float x[8];
-      float mx = -INFINITY;
+      mx[nt] = -INFINITY;
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int t = t0 + 8 * q + 4 * st + i;
-          const float v = s[st][nt][i] * p.scale_log2;
-          x[4 * st + i] = (t < nvis[nt]) ? v : -INFINITY;
-          mx = fmaxf(mx, x[4 * st + i]);
+          float v = s[st][nt][i] * p.scale_log2;
+          if (masked) v = (t0 + 8 * q + 4 * st + i < nvis[nt]) ? v : -INFINITY;
+          x[nt][4 * st + i] = v;
+          mx[nt] = fmaxf(mx[nt], v);
         }
-      mx = wave_max_xor16_32(mx);
-      const float m_new = fmaxf(m_run[nt], mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2f(m_run[nt] - m_use);
+      mx[nt] = wave_max_xor16_32(mx[nt]);
+    }
+    bool resc = false;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) resc |= mx[nt] > m_run[nt] + 8.f;
+    if (__any(resc)) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const float m_new = fmaxf(m_run[nt], mx[nt]);
+        const float alpha = (m_run[nt] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[nt] - m_new);
+        l_run[nt] *= alpha;
+        m_run[nt] = m_new;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) o[mt][nt] *= alpha;
+      }
+    }
+    bf16x8 pb[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const float m_use = (m_run[nt] == -INFINITY) ? 0.f : m_run[nt];
       float ps = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        x[j] = exp2f(x[j] - m_use);
-        ps += x[j];
+        x[nt][j] = __builtin_amdgcn_exp2f(x[nt][j] - m_use);
+        ps += x[nt][j];
       }
-      l_run[nt] = l_run[nt] * alpha + ps;
-      m_run[nt] = m_new;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) o[mt][nt] *= alpha;
-      u32x4 pk = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
-                  pack_bf16x2(x[6], x[7])};
+      l_run[nt] += ps;
+      u32x4 pk = {pack_bf16x2(x[nt][0], x[nt][1]), pack_bf16x2(x[nt][2], x[nt][3]),
+                  pack_bf16x2(x[nt][4], x[nt][5]), pack_bf16x2(x[nt][6], x[nt][7])};
       pb[nt] = __builtin_bit_cast(bf16x8, pk);
     }
     // tokens past the end of the sequence may hold anything: keep their V at 0
