@@ -95,9 +95,13 @@ struct AbsorbCfg {
 };
 
 // Swizzle of 16-byte chunk positions inside a token row (tokens 0..31 of a
-// tile): conflict-free for both the QK reads (16 tokens, one chunk) and the
-// transposed PV reads (4 tokens x 2 chunks per 16-lane group).
-__device__ __forceinline__ int tile_swz(int t) { return 4 * ((t >> 1) & 1) + (t >> 3); }
+// tile).  gfx950 LDS has 64 four-byte banks; a 16-byte read is served in four
+// passes of 16 lanes (per half wave, the 4-lane quads of even and of odd bit
+// parity), an 8-byte or transposing read in two passes of 32 lanes.  With a
+// 1152-byte token row, XOR-ing chunk bits 1 and 2 with token bits 1 and 3
+// gives every pass of the QK reads (16 tokens, one chunk) and of the
+// transposing PV reads (8 tokens x 4 half-chunks) 64 distinct banks.
+__device__ __forceinline__ int tile_swz(int t) { return 4 * ((t >> 3) & 1) + 2 * ((t >> 1) & 1); }
 
 template <int HPG, int SQ, int R, int DR, int DN, int DV>
 __global__ __launch_bounds__(512, 1) void absorb_decode_kernel(DecodeParams p) {

@@ -55,8 +55,11 @@ struct GqaCfg {
 // {8a + 4st + b} (a, b in 0..3) at one chunk: kswz is distinct over them.
 __device__ __forceinline__ int kswz(int t) { return (t & 3) | ((t >> 3) << 2); }
 __device__ __forceinline__ int rswz(int t) { return ((t >> 1) & 1) | ((t >> 3) << 1); }
-// V^T rows d: 16 consecutive rows, one chunk -> distinct (d%4, chunk) bank groups.
-__device__ __forceinline__ int vswz(int d) { return (d >> 2) & 3; }
+// V^T rows d (64 bytes): a 16-byte read is served in four passes of 16 lanes
+// (per half wave, the 4-lane quads of even and of odd bit parity) over 64
+// four-byte banks; XOR-ing chunk bit 1 with row bit 2 makes every pass of the
+// PV reads (16 rows, chunks q) hit 64 distinct banks.
+__device__ __forceinline__ int vswz(int d) { return 2 * ((d >> 2) & 1); }
 
 template <int HPG, int SQ, int DN, int DV, int DR>
 __global__ __launch_bounds__(64) void gqa_decode_kernel(DecodeParams p) {
