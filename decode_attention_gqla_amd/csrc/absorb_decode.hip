@@ -2,7 +2,7 @@
 //
 // GQLA pages: paperlayer.ai summary, section 4 "MQA-absorb path" and
 // gist.science section 2 "MQA-Absorb-Pfad": W_UK[G] is folded into the query
-// of every head, all h_q heads attend over the latent cache c^KV_t ++ k^R_t
+// of every head, all h_q heads attend over the latent cache c^KV_t ++ k_rope_t
 // (read once and shared by every query row), and W_UV[G] up-projects the
 // latent output.  Per query row (head h in group G, MTP row i):
 //   q_abs = W_UK[G] q_nope,   s_t = (q_abs . c_t + q_rope . k_rope_t) * scale,
@@ -12,37 +12,45 @@
 //   1. absorb_q_kernel: q_abs for every query row of the batch (a per-group
 //      [rows x d_nope] x [d_nope x r] MFMA product), stored with q_rope as one
 //      bf16 row of r + d_R in the workspace;
-//   2. wuv_transpose_kernel: W_UV^T into the workspace (so the up-projection
-//      reads its operand rows contiguously);
-//   3. absorb_decode_kernel: attention + up-projection, one workgroup of 8
-//      waves per (split of a sequence, block of 64 query rows).  The row
-//      blocks of one split run side by side on one XCD, so each cache byte is
-//      fetched from HBM once and re-read from that XCD's L2.
+//   2. wuv_transpose_kernel: W_UV^T into the workspace, its latent index
+//      permuted inside each 32-wide block to the order in which the decode
+//      kernel's accumulators hold o_lat (see the epilogue);
+//   3. absorb_decode_kernel: attention + up-projection, one workgroup of four
+//      waves (one per SIMD, so each wave may hold 512 registers) per (split
+//      of a sequence, block of 128 query rows).
 //
-// Inside the decode kernel each 32-token latent tile is copied HBM -> LDS by
-// direct DMA (global_load_lds_dwordx4, three tiles in flight) into a
-// XOR-swizzled token-major layout, and the 8 waves split the work so that
-// the query operands (64 rows x 576) and the output accumulators
-// (64 rows x 512 fp32) sit in registers with room to spare:
-//   QK      wave (16-row tile rt, half kh): S^T over half of the 576-wide
-//           contraction; the two halves are summed through LDS;
-//   softmax waves 0..3 own one 16-row tile each: online softmax, P (bf16)
-//           to LDS;
-//   PV      wave w owns latent dims [64w, 64w + 64) of all 64 rows:
-//           O^T[latent][row] += C^T . P^T, with C^T read by the LDS
-//           transposing read ds_read_b64_tr_b16 once and reused for the 4
-//           16-row tiles.
-// Epilogue: o_lat (bf16) staged in LDS; wave w up-projects half of the
-// output dims of one 16-row tile: out^T = W_UV^T o_lat^T on MFMA.
+// Decode kernel.  Each 32-token latent tile (36 KB for r + d_R = 576) is
+// copied HBM -> LDS by direct DMA (global_load_lds_dwordx4; four tile
+// buffers, tiles it+1 and it+2 in flight while tile it is used) into a
+// XOR-swizzled token-major layout.  Wave w owns 32 query rows end to end:
+//   * its query rows (two 16-row tiles x the full 576-wide contraction) stay
+//     in registers as MFMA B operands;
+//   * S^T = C_tile . Q^T: each 16-token x 32-dim cache operand read from LDS
+//     feeds two MFMAs (the two row tiles);
+//   * online softmax inside the wave: the token order of a tile is relabelled
+//     so that the S^T accumulators are exactly the P^T B operands of the PV
+//     product, so P never leaves registers;
+//   * O^T[latent][row] += C^T P^T over all 512 latent dims: the O
+//     accumulators (32 rows x 512 fp32) live in the accumulation registers;
+//     each C^T operand is read by the transposing LDS read ds_read_b64_tr_b16
+//     and feeds two MFMAs.
+// One workgroup barrier per tile (copies landed, and the buffer refilled next
+// has been read by every wave).  The PV product of tile it-1 runs in the same
+// iteration as QK of tile it, so the MFMA units see both streams, and the
+// copies of tile it+2 are issued one instruction at a time between QK steps.
+// Epilogue: o_lat is normalised, rounded to bf16 and fed straight from the
+// accumulators into out^T = W_UV^T o_lat^T on MFMA (no LDS staging).
+#include <type_traits>
+
 #include "common.hip.h"
 #include "params.hip.h"
 
 namespace gqla {
 
+// Workgroup barrier for LDS hand-offs: this wave's LDS reads and writes are
+// complete before it arrives.
 __device__ __forceinline__ void block_sync_lds() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Outstanding-copy counts are wave-uniform but not compile-time constants.
@@ -51,6 +59,7 @@ __device__ __forceinline__ void vm_wait_dyn(int n) {
 #define GQLA_WV(N) case N: vm_wait<N>(); break;
     GQLA_WV(0) GQLA_WV(1) GQLA_WV(2) GQLA_WV(3) GQLA_WV(4) GQLA_WV(5) GQLA_WV(6) GQLA_WV(7)
     GQLA_WV(8) GQLA_WV(9) GQLA_WV(10) GQLA_WV(11) GQLA_WV(12) GQLA_WV(13) GQLA_WV(14) GQLA_WV(15)
+    GQLA_WV(16) GQLA_WV(17) GQLA_WV(18) GQLA_WV(19) GQLA_WV(20) GQLA_WV(21) GQLA_WV(22) GQLA_WV(23)
 #undef GQLA_WV
     default: vm_wait<0>(); break;
   }
@@ -60,38 +69,29 @@ template <int HPG, int SQ, int R, int DR, int DN, int DV>
 struct AbsorbCfg {
   static constexpr int BS = 64;
   static constexpr int TILE = 32;                 // tokens per LDS tile
-  static constexpr int NBUF = 3;
+  static constexpr int NBUF = 4;                  // tile buffers
   static constexpr int ROW = R + DR;              // latent row (elements)
   static constexpr int CHR = ROW / 8;             // 16-byte chunks per token row
   static constexpr bool SWZ = (CHR % 8) == 0;     // XOR swizzle stays inside a row
   static constexpr int BUF_BYTES = TILE * ROW * 2;
   static constexpr int NI = TILE * CHR / 64;      // wave-wide DMA instructions per tile
-  static constexpr int NW = 8;                    // waves per workgroup
-  static constexpr int ROWS_WG = 64;              // query rows per workgroup (4 n-tiles)
-  static constexpr int NTW = ROWS_WG / 16;        // 16-row tiles per workgroup
+  static constexpr int NW = 4;                    // waves per workgroup (one per SIMD)
+  static constexpr int NIW = (NI + NW - 1) / NW;  // most DMA instructions of one wave per tile
+  static constexpr int NTW = 1;                   // 16-row tiles per wave
+  static constexpr int ROWS_W = 16 * NTW;         // query rows per wave
+  static constexpr int ROWS_WG = NW * ROWS_W;
   static constexpr int KSL = R / 32;              // k steps over the latent
   static constexpr int KSR = (DR + 31) / 32;      // k steps over the rope key (zero padded)
   static constexpr int KS = KSL + KSR;
-  static constexpr int KSH = (KS + 1) / 2;        // k steps per half
   static constexpr int MTL = R / 16;              // 16-dim tiles of o_lat
-  static constexpr int MTW = MTL >= NW ? MTL / NW : 1;   // latent tiles per wave in PV
   static constexpr int MD = DV / 16;              // 16-dim tiles of the output
-  // LDS map (bytes)
-  static constexpr int OFF_SP = NBUF * BUF_BYTES;            // partial S: [2][NTW][2][64] f32x4
-  static constexpr int OFF_PB = OFF_SP + 2 * NTW * 2 * 64 * 16;     // P: [NTW][64] bf16x8
-  static constexpr int OFF_AL = OFF_PB + NTW * 64 * 16;      // alpha per row [ROWS_WG] f32
-  static constexpr int OFF_FL = OFF_AL + ROWS_WG * 4;        // rescale flag per n-tile i32
-  static constexpr int OFF_IL = OFF_FL + 64;                 // 1/l per row [ROWS_WG] f32
-  static constexpr int LDS_BYTES = OFF_IL + ROWS_WG * 4;
-  static constexpr int OLAT_BYTES = ROWS_WG * R * 2;         // epilogue staging (overlaps KV/SP)
-  static constexpr int OSWZ = (R / 8) >= 16 ? 15 : (R / 8) - 1;   // o_lat chunk swizzle mask
-  static_assert(OLAT_BYTES <= OFF_AL, "o_lat staging must not overlap the row arrays");
+  static constexpr int OFF_FLAG = NBUF * BUF_BYTES;          // restart request (int)
+  static constexpr int LDS_BYTES = OFF_FLAG + 16;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert((TILE * CHR) % 64 == 0, "tile must be whole DMA instructions");
   static_assert(R % 32 == 0 && DN % 32 == 0 && DV % 16 == 0, "unsupported dims");
-  static_assert(MTL % NW == 0 || MTL < NW, "latent tiles must split evenly over waves");
-  static_assert(!SWZ || MTW % 4 == 0, "swizzled PV addressing needs 4 tiles per wave");
-  static_assert((NI + NW - 1) / NW <= 15, "vmcnt budget");
-  static_assert(NW == 2 * NTW, "one QK wave per (n-tile, contraction half)");
+  static_assert(!SWZ || MTL % 4 == 0, "swizzled PV addressing takes latent tiles in fours");
+  static_assert(NIW <= 23, "vmcnt budget");
 };
 
 // Swizzle of 16-byte chunk positions inside a token row (tokens 0..31 of a
@@ -104,10 +104,11 @@ struct AbsorbCfg {
 __device__ __forceinline__ int tile_swz(int t) { return 4 * ((t >> 3) & 1) + 2 * ((t >> 1) & 1); }
 
 template <int HPG, int SQ, int R, int DR, int DN, int DV>
-__global__ __launch_bounds__(512, 1) void absorb_decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void absorb_decode_kernel(DecodeParams p) {
   using C = AbsorbCfg<HPG, SQ, R, DR, DN, DV>;
   constexpr int BS = C::BS, ROW = C::ROW, CHR = C::CHR, KSL = C::KSL, KS = C::KS;
-  constexpr int KSH = C::KSH, MTW = C::MTW, MD = C::MD, MTL = C::MTL;
+  constexpr int MD = C::MD, MTL = C::MTL, NW = C::NW, NTW = C::NTW;
   __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[C::LDS_BYTES];
   lds_u8_t* const lds = (lds_u8_t*)lds_raw;
 
@@ -115,6 +116,8 @@ __global__ __launch_bounds__(512, 1) void absorb_decode_kernel(DecodeParams p) {
   const int H = HPG * g;
   const int rows_total = H * SQ;
   const int RB = (rows_total + C::ROWS_WG - 1) / C::ROWS_WG;
+  // Workgroups are dispatched round-robin over the 8 XCDs; the row blocks of
+  // one split unit take consecutive slots on one XCD (shared L2).
   const int wg = blockIdx.x;
   const int xcd = wg & 7, k = wg >> 3;
   const int u = (k / RB) * 8 + xcd;
@@ -141,299 +144,357 @@ __global__ __launch_bounds__(512, 1) void absorb_decode_kernel(DecodeParams p) {
   const int L = __builtin_amdgcn_readfirstlane(p.seqlens[b]);
   const int n_tiles = hi > lo ? (hi - lo + C::TILE - 1) / C::TILE : 0;
   const int32_t* bt = p.block_table + (size_t)b * p.max_blocks;     // wave-uniform
-  const int row_base = rb * C::ROWS_WG;           // first query row of this workgroup
 
-  // ---- HBM -> LDS tile copy (each wave issues instructions w, w+8, ...) ----
-  const int niw = (C::NI - w + C::NW - 1) / C::NW;
-  auto issue_tile = [&](int it) {
+  // ---- HBM -> LDS tile copies: wave w issues instructions w, w+4, ... ----
+  // Block-table entries are read through the scalar cache (constant address
+  // space, wave-uniform index).  The per-lane source offsets of this wave's
+  // copy instructions are the same for every tile and are computed once.
+  typedef const __attribute__((address_space(4))) int32_t cint32_t;
+  const cint32_t* const cbt = (const cint32_t*)bt;
+  constexpr bool kFixedCopies = (C::NI % NW) == 0;   // every wave issues NIW copies per tile
+  const int niw = kFixedCopies ? C::NIW : (C::NI - w + NW - 1) / NW;
+  uint32_t dvo[C::NIW];
+#pragma unroll
+  for (int kk = 0; kk < C::NIW; ++kk) {
+    const int i = min(w + NW * kk, C::NI - 1);
+    const int P = i * 64 + lane;
+    const int t = P / CHR, pos = P % CHR;
+    const int ch = C::SWZ ? (pos ^ tile_swz(t)) : pos;
+    dvo[kk] = (uint32_t)(t * ROW + ch * 8) * 2u;
+    asm volatile("" : "+v"(dvo[kk]));             // keep, do not recompute per tile
+  }
+  struct Copy {
+    const uint16_t* src;
+    lds_u8_t* dst;
+  };
+  auto copy_of = [&](int it) -> Copy {
     const int t0 = lo + C::TILE * it;
-    const uint16_t* src = p.cache + ((size_t)sload_i32(bt + t0 / BS) * BS + (t0 % BS)) * ROW;
-    lds_u8_t* dst = lds + (it % C::NBUF) * C::BUF_BYTES;
-    for (int i = w; i < C::NI; i += C::NW) {
-      const int P = i * 64 + lane;
-      const int t = P / CHR, pos = P % CHR;
-      const int ch = C::SWZ ? (pos ^ tile_swz(t)) : pos;
-      dma16(src, (uint32_t)(t * ROW + ch * 8) * 2u, dst + i * 1024);
-    }
+    const int page = cbt[t0 / BS];
+    return Copy{p.cache + ((size_t)page * BS + (t0 % BS)) * ROW, lds + (it % C::NBUF) * C::BUF_BYTES};
+  };
+  auto copy_part = [&](const Copy& cp, int kk) {  // instruction kk of this wave (kk < niw)
+    dma16(cp.src, dvo[kk], cp.dst + (w + NW * kk) * 1024);
   };
 
-  // ---- QK role: 16-row tile rt, k steps [kh*KSH, kh*KSH + KSH) ----
-  const int rt = w >> 1, kh = w & 1;
-  bf16x8 qb[KSH];
-  {
-    const int rho = row_base + 16 * rt + c;
+  // ---- this wave's query rows: tiles nt < NTW of rows row0 + 16 nt + c ----
+  const int row0 = rb * C::ROWS_WG + C::ROWS_W * w;
+  const bool active = row0 < rows_total;          // wave-uniform
+  const bool rows_all_valid = row0 + C::ROWS_W <= rows_total;
+  bf16x8 qb[NTW][KS];
+  int s_nvis[NTW];
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    const int rho = row0 + 16 * nt + c;
     const bool valid = rho < rows_total;
     const int h = valid ? rho / SQ : 0, i = valid ? rho % SQ : 0;
+    s_nvis[nt] = valid ? L - SQ + i + 1 : -1;
     const uint16_t* qrow = p.qcat + (((size_t)b * SQ + i) * H + h) * ROW;
 #pragma unroll
-    for (int j = 0; j < KSH; ++j) {
-      const int dim = 32 * (kh * KSH + j) + 8 * q;
-      qb[j] = (valid && kh * KSH + j < KS && dim < ROW) ? ld_bf16x8(qrow + dim) : zero_bf16x8();
+    for (int ks = 0; ks < KS; ++ks) {
+      const int dim = 32 * ks + 8 * q;
+      qb[nt][ks] = (valid && dim < ROW) ? ld_bf16x8(qrow + dim) : zero_bf16x8();
     }
   }
-  // ---- softmax role (waves 0 .. NTW-1): rows 16*w .. 16*w+15 of the block ----
-  const bool smax_wave = w < C::NTW;
-  const int srow = 16 * (w % C::NTW) + c;         // block-local row of this lane
-  const int srho = row_base + srow;
-  const bool svalid = smax_wave && srho < rows_total;
-  const int s_nvis = svalid ? L - SQ + (srho % SQ) + 1 : -1;
-  float m_run = -INFINITY, l_run = 0.f;
 
-  // Per-lane LDS byte offsets of the MFMA operands inside a tile buffer,
-  // recomputed each tile from an opaque zero (cheaper than keeping a dozen
-  // loop-invariant registers live across the tile loop).
-  // QK: token t = 8*(c/4) + 4*st + c%4, chunk 4ks + q, which sits at
-  // 4*(ks ^ s2) + (q ^ (sw & 3)) with sw = tile_swz(t), s2 = sw >> 2: one base
-  // per ks parity, the rest an immediate offset.
-  auto qk_base = [&](int z, int st, int par) -> int {
-    const int t = 8 * (c >> 2) + 4 * st + (c & 3) + z;
-    const int sw = C::SWZ ? tile_swz(t) : 0;
-    const int lowq = q ^ (sw & 3), s2 = sw >> 2;
-    return (t * CHR + lowq + 4 * (par == 0 ? s2 : -s2)) * 16;
-  };
-  // PV (transposing reads): tokens t = 8q + c/4 (+4), latent 16mt + 4*(c%4),
-  // chunk 2mt + b1 at 2*((mt & ~3) | ((mt & 3) ^ s1)) + (b1 ^ (sw & 1)).
-  auto pv_base = [&](int z, int hh, int m3) -> int {
-    const int t = 8 * q + (c >> 2) + 4 * hh + z;
-    const int sw = C::SWZ ? tile_swz(t) : 0;
-    const int b1 = (c & 3) >> 1, half = ((4 * (c & 3)) & 7) * 2;
-    return (t * CHR + 2 * (m3 ^ (sw >> 1)) + (b1 ^ (sw & 1))) * 16 + half;
-  };
-  const int mt0 = w * MTW;                        // first latent tile of this wave (PV)
-  const bool pv_active = mt0 < MTL;
-
-  constexpr int NTW = C::NTW;
-  f32x4 o[MTW][NTW];
+  // Per-lane LDS byte offsets of the MFMA operands inside a tile buffer
+  // (computed once; each read adds the buffer's offset and an immediate).
+  // QK operand of token half st: token t = 8*(c/4) + 4*st + c%4, chunk
+  // 4ks + q, which sits at 4*(ks ^ s2) + (q ^ (sw & 3)) with sw = tile_swz(t),
+  // s2 = sw >> 2: one base per (st, ks parity), the rest is 64 ks bytes.
+  int qkb[2][2];
 #pragma unroll
-  for (int j = 0; j < MTW; ++j)
+  for (int st = 0; st < 2; ++st)
 #pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) o[j][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int par = 0; par < 2; ++par) {
+      const int t = 8 * (c >> 2) + 4 * st + (c & 3);
+      const int sw = C::SWZ ? tile_swz(t) : 0;
+      const int lowq = q ^ (sw & 3), s2 = sw >> 2;
+      qkb[st][par] = (t * CHR + lowq + 4 * (par == 0 ? s2 : -s2)) * 16;
+      asm volatile("" : "+v"(qkb[st][par]));
+    }
+  // PV operand (transposing reads), half hh: tokens t = 8q + c/4 + 4hh, latent
+  // 16mt + 4*(c%4), i.e. chunk 2mt + b1 (b1 = (c%4)/2), which the swizzle puts
+  // at 2*((mt & ~3) | ((mt & 3) ^ (sw >> 1))) + (b1 ^ (sw & 1)): one base per
+  // (hh, mt % 4), the rest is 128 (mt / 4) bytes; unswizzled, 32 mt bytes.
+  constexpr int NPV = C::SWZ ? 4 : 1;
+  int pvb[2][NPV];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int m3 = 0; m3 < NPV; ++m3) {
+      const int t = 8 * q + (c >> 2) + 4 * hh;
+      const int sw = C::SWZ ? tile_swz(t) : 0;
+      const int b1 = (c & 3) >> 1, half = ((4 * (c & 3)) & 7) * 2;
+      pvb[hh][m3] = (t * CHR + 2 * (m3 ^ (sw >> 1)) + (b1 ^ (sw & 1))) * 16 + half;
+      asm volatile("" : "+v"(pvb[hh][m3]));
+    }
+  auto pv_operand = [&](const lds_u8_t* buf, int mt) -> bf16x8 {
+    const int m3 = C::SWZ ? (mt & 3) : 0;
+    const int imm = C::SWZ ? 128 * (mt >> 2) : 32 * mt;
+    const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(buf + pvb[0][m3] + imm));
+    const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(buf + pvb[1][m3] + imm));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
 
-  // The query loads complete before the first tile copy is issued, so the
+  // Softmax reference.  A row's reference is its first finite tile maximum
+  // and then stays fixed, so the O accumulators are only ever written by
+  // MFMAs (an in-place rescale of the accumulation registers would need a
+  // second register set).  Every p = 2^(x - ref) is kept below 2^kSlack; a
+  // tile maximum above ref + kSlack (an extreme logit spread, e.g. one
+  // dominant token) makes the workgroup restart the split: pass 1 sweeps QK
+  // for the exact row maxima, pass 2 reruns the attention with them as the
+  // references (then p <= 1).
+  constexpr float kSlack = 64.f;
+  f32x4 o[MTL][NTW];                              // O^T: lane (q, c) = latent 16mt + 4q.., row c
+  float m_run[NTW], l_run[NTW];
+  bf16x8 pb[NTW];                                 // P^T operands of the previous tile
+  int* const restart_flag = (int*)(lds_raw + C::OFF_FLAG);
+  if (tid == 0) *restart_flag = 0;                // ordered before its reads by the first barrier
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) m_run[nt] = -INFINITY;
+
+  // The query loads complete before the first copy is issued, so the
   // compiler's own wait tracking has nothing pending inside the tile loop.
   vm_wait<0>();
-  if (n_tiles > 0) issue_tile(0);
-  if (n_tiles > 1) issue_tile(1);
-
-  lds_u8_t* const sp = lds + C::OFF_SP;
-  lds_u8_t* const pbuf = lds + C::OFF_PB;
-  float* const al = (float*)(lds_raw + C::OFF_AL);
-  int* const fl = (int*)(lds_raw + C::OFF_FL);
-
-  for (int it = 0; it < n_tiles; ++it) {
-    // tile it landed (own copies), then for every wave
-    if (it + 1 < n_tiles) vm_wait_dyn(niw); else vm_wait<0>();
-    block_sync_lds();
-    const lds_u8_t* buf = lds + (it % C::NBUF) * C::BUF_BYTES;
-    const int t0 = lo + C::TILE * it;
-    int z;                                        // opaque 0: keeps per-lane offsets in the loop
-    asm volatile("v_mov_b32 %0, 0" : "=v"(z));
-
-    // ---- QK (half of the contraction), partial S^T to LDS ----
-    {
-      auto qk_operand = [&](int st, int j) -> bf16x8 {
-        const int ks = kh * KSH + j;              // wave-uniform
-        const bool have = ks < KS && (ks < KSL || 32 * (ks - KSL) + 8 * q < DR);
-        if (!have) return zero_bf16x8();
-        const int off = qk_base(z, st, C::SWZ ? (ks & 1) : 0) + 64 * ks;
-        return __builtin_bit_cast(bf16x8, *(const lds_u32x4_t*)(buf + off));
-      };
-      // one token subtile at a time, operands read three steps ahead; the
-      // compiler barrier per step keeps the remaining reads from being hoisted
+  for (int pass = 0; pass < 3; ++pass) {          // 0: single pass; 1, 2: after a restart
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        f32x4 s0 = {0.f, 0.f, 0.f, 0.f};
-        constexpr int PD = 3;
+    for (int nt = 0; nt < NTW; ++nt) {
+#pragma unroll
+      for (int mt = 0; mt < MTL; ++mt) o[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      l_run[nt] = 0.f;
+      pb[nt] = zero_bf16x8();
+    }
+    for (int i = 0; i < 2 && i < n_tiles; ++i) {
+      const Copy cp = copy_of(i);
+      for (int kk = 0; kk < niw; ++kk) copy_part(cp, kk);
+    }
+    bool restart = false;
+    for (int it = 0; it <= n_tiles; ++it) {
+      // tile it landed (own copies; tile it+1 may still be in flight), then
+      // for every wave; every wave is also past PV of tile it-2, whose buffer
+      // takes tile it+2
+      if (it + 1 < n_tiles) {
+        if constexpr (kFixedCopies) vm_wait<C::NIW>(); else vm_wait_dyn(niw);
+      } else {
+        vm_wait<0>();
+      }
+      block_sync_lds();
+      // a restart request posted before this barrier (pass 0 only)
+      const int flag = pass == 0 ? *(volatile int*)restart_flag : 0;
+      if (it < n_tiles && lo + C::TILE * (it + 1) > L) {
+        // the sequence's last tile: token rows past its end hold anything
+        // (the page's unused slots); zero them so the PV product needs no
+        // mask (their logits are masked, but 0 * NaN would still be NaN)
+        const int valid = L - (lo + C::TILE * it);
+        lds_u8_t* buf = lds + (it % C::NBUF) * C::BUF_BYTES;
+        for (int off = valid * ROW * 2 + tid * 16; off < C::BUF_BYTES; off += 64 * NW * 16)
+          *(lds_u32x4_t*)(buf + off) = u32x4{0u, 0u, 0u, 0u};
+        block_sync_lds();
+      }
+      const bool more = it + 2 < n_tiles;
+      Copy cp = {nullptr, nullptr};
+      if (more) cp = copy_of(it + 2);
+
+      // ---- S^T of tile it: 2 token halves x NTW row tiles, full contraction ----
+      // With a fixed copy count per wave, the copies of tile it+2 are issued
+      // one at a time between QK steps (two copies of the unrolled QK body,
+      // with and without them, so no runtime branch sits between the MFMAs);
+      // otherwise they all go out after QK.
+      f32x4 s[2][NTW];
+      auto qk_tile = [&](auto with_copies) {
+        constexpr bool WITH = decltype(with_copies)::value;
+        const lds_u8_t* buf = lds + (it % C::NBUF) * C::BUF_BYTES;
+        auto qk_operand = [&](int step) -> bf16x8 {  // step = 2 ks + st
+          const int ks = step >> 1, st = step & 1;
+          const bool have = ks < KSL || 32 * (ks - KSL) + 8 * q < DR;
+          if (!have) return zero_bf16x8();
+          return __builtin_bit_cast(bf16x8,
+                                    *(const lds_u32x4_t*)(buf + qkb[st][C::SWZ ? (ks & 1) : 0] + 64 * ks));
+        };
+        constexpr int NS = 2 * KS, PD = 6;
+        constexpr int GAP = NS / (C::NIW + 1) > 0 ? NS / (C::NIW + 1) : 1;   // QK steps between copies
         bf16x8 a[PD + 1];
 #pragma unroll
-        for (int j = 0; j < PD && j < KSH; ++j) a[j] = qk_operand(st, j);
+        for (int j = 0; j < PD && j < NS; ++j) a[j] = qk_operand(j);
 #pragma unroll
-        for (int j = 0; j < KSH; ++j) {
-          if (j + PD < KSH) a[(j + PD) % (PD + 1)] = qk_operand(st, j + PD);
-          s0 = mfma16(a[j % (PD + 1)], qb[j], s0);
-          asm volatile("" ::: "memory");
+        for (int j = 0; j < NS; ++j) {
+          if (j + PD < NS) a[(j + PD) % (PD + 1)] = qk_operand(j + PD);
+          const int ks = j >> 1, st = j & 1;
+#pragma unroll
+          for (int nt = 0; nt < NTW; ++nt)
+            s[st][nt] = mfma16(a[j % (PD + 1)], qb[nt][ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[st][nt]);
+          if (WITH && j % GAP == GAP - 1 && j / GAP < C::NIW) copy_part(cp, j / GAP);   // folded at compile time
         }
-        *(__attribute__((address_space(3))) f32x4*)(sp + (((kh * NTW + rt) * 2 + st) * 64 + lane) * 16) = s0;
+        // schedule: the first PD operand reads, then per step the read of
+        // operand j + PD followed by the MFMA(s) of step j
+        __builtin_amdgcn_sched_group_barrier(0x100, PD < NS ? PD : NS, 0);
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+          if (j + PD < NS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, NTW, 0);
+        }
+      };
+      int issued = 0;
+      if (it < n_tiles && active) {
+        if (kFixedCopies && more) {
+          qk_tile(std::true_type{});
+          issued = niw;
+        } else {
+          qk_tile(std::false_type{});
+        }
       }
-    }
-    block_sync_lds();
-    // every wave is past PV of tile it-1: its buffer can be refilled
-    if (it + 2 < n_tiles) issue_tile(it + 2);
+      if (more)
+        for (; issued < niw; ++issued) copy_part(cp, issued);
+      if (__builtin_amdgcn_readfirstlane(flag)) { // uniform over the workgroup
+        restart = true;
+        break;
+      }
 
-    // ---- softmax for rows 16w .. 16w+15 (waves 0 .. NTW-1) ----
-    if (smax_wave) {
-      // masking is needed only on tiles that reach the first causal bound
-      const bool masked = t0 + C::TILE > L - SQ + 1 || !svalid;
-      float x[8];
-      float mx = -INFINITY;
+      // ---- O^T += C^T P^T for tile it-1 ----
+      if (pass != 1 && it > 0 && active) {
+        const lds_u8_t* buf = lds + ((it - 1) % C::NBUF) * C::BUF_BYTES;
+        constexpr int PV = 6;                     // operands read ahead
+        bf16x8 v[PV + 1];
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const int base = (w * 2 + st) * 64 + lane;            // half 0 of (n-tile w, st)
-        const f32x4 a0 = *(const __attribute__((address_space(3))) f32x4*)(sp + base * 16);
-        const f32x4 a1 = *(const __attribute__((address_space(3))) f32x4*)(sp + (base + NTW * 2 * 64) * 16);
+        for (int j = 0; j < PV && j < MTL; ++j) v[j] = pv_operand(buf, j);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = (a0[i] + a1[i]) * p.scale_log2;
-          if (masked) v = (t0 + 8 * q + 4 * st + i < s_nvis) ? v : -INFINITY;
-          x[4 * st + i] = v;
-          mx = fmaxf(mx, v);
+        for (int mt = 0; mt < MTL; ++mt) {
+          if (mt + PV < MTL) v[(mt + PV) % (PV + 1)] = pv_operand(buf, mt + PV);
+#pragma unroll
+          for (int nt = 0; nt < NTW; ++nt) o[mt][nt] = mfma16(v[mt % (PV + 1)], pb[nt], o[mt][nt]);
+        }
+        // schedule: the first PV operands' reads, then per step the reads of
+        // operand mt + PV followed by the MFMA(s) of step mt
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (PV < MTL ? PV : MTL), 0);
+#pragma unroll
+        for (int mt = 0; mt < MTL; ++mt) {
+          if (mt + PV < MTL) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, NTW, 0);
         }
       }
-      mx = wave_max_xor16_32(mx);
-      // lazily moved reference max: rescale only when it grows by more than 8
-      // (so every p <= 2^8), which after the first tiles is rare
-      const bool resc = __any(mx > m_run + 8.f);
-      if (resc) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-        m_run = m_new;
-        if (q == 0) al[srow] = alpha;
-      }
-      if (lane == 0) fl[w] = resc ? 1 : 0;
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      float ps = 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        x[j] = __builtin_amdgcn_exp2f(x[j] - m_use);
-        ps += x[j];
-      }
-      l_run += ps;
-      u32x4 pk = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
-                  pack_bf16x2(x[6], x[7])};
-      *(lds_u32x4_t*)(pbuf + (w * 64 + lane) * 16) = pk;
-    }
-    block_sync_lds();
+      if (it == n_tiles) break;
 
-    // ---- PV for latent tiles mt0 .. mt0+MTW-1 of all the block's rows ----
-    if (pv_active) {
-      int flags[NTW];
-#pragma unroll
-      for (int nt = 0; nt < NTW; nt += 4) {
-        const u32x4 f4 = *(const lds_u32x4_t*)(lds + C::OFF_FL + nt * 4);
-#pragma unroll
-        for (int k2 = 0; k2 < 4 && nt + k2 < NTW; ++k2) flags[nt + k2] = (int)f4[k2];
-      }
-#pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) {
-        if (flags[nt]) {                          // rows of n-tile nt moved their reference
-          const float a = al[16 * nt + c];
-#pragma unroll
-          for (int j = 0; j < MTW; ++j) o[j][nt] *= a;
-        }
-      }
-      const bool tail = t0 + C::TILE > L;
-      const int keep = min(max(L - (t0 + 8 * q), 0), 8);
-      // latent tiles two at a time (8 operand registers), P tiles re-read per pair
-      constexpr int JP = MTW >= 2 ? 2 : 1;
-#pragma unroll
-      for (int j0 = 0; j0 < MTW; j0 += JP) {
-        bf16x8 v[JP];
-#pragma unroll
-        for (int jj = 0; jj < JP; ++jj) {
-          const int j = j0 + jj, mt = mt0 + j;
-          if constexpr (C::SWZ) {
-            const int off_lo = pv_base(z, 0, j & 3) + 128 * (mt >> 2);
-            const int off_hi = pv_base(z, 1, j & 3) + 128 * (mt >> 2);
-            s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(buf + off_lo));
-            s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(buf + off_hi));
-            v[jj] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-          } else {
-            const int n = 16 * mt + 4 * (c & 3);
-            const int ch = n >> 3, half = (n & 7) * 2;
-            const int t_lo = 8 * q + (c >> 2), t_hi = t_lo + 4;
-            s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(buf + (t_lo * CHR + ch) * 16 + half));
-            s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(buf + (t_hi * CHR + ch) * 16 + half));
-            v[jj] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-          }
-          if (tail) v[jj] = keep_first(v[jj], keep);   // tokens past the sequence end hold anything
-        }
+      // ---- softmax of tile it (base 2), per row tile ----
+      if (active) {
+        const int t0 = lo + C::TILE * it;
+        // masking is needed only on tiles that reach the first causal bound
+        const bool masked = t0 + C::TILE > L - SQ + 1 || !rows_all_valid;
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) {
-          const bf16x8 pbv = __builtin_bit_cast(bf16x8, *(const lds_u32x4_t*)(pbuf + (nt * 64 + lane) * 16));
+          // lane (q, c): tokens t0 + 8q + 4st + i of row c (st = 0, 1; i = 0..3)
+          float x[8];
 #pragma unroll
-          for (int jj = 0; jj < JP; ++jj) o[j0 + jj][nt] = mfma16(v[jj], pbv, o[j0 + jj][nt]);
+          for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[4 * st + i] = s[st][nt][i] * p.scale_log2;
+          if (masked) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              x[j] = (t0 + 8 * q + 4 * (j >> 2) + (j & 3) < s_nvis[nt]) ? x[j] : -INFINITY;
+          }
+          float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+          mx = wave_max_q(mx);
+          if (pass == 1) {                        // exact row maxima only
+            m_run[nt] = fmaxf(m_run[nt], mx);
+            continue;
+          }
+          if (pass == 0) {
+            // a row takes its first finite tile maximum as its reference (its
+            // O and l are still 0); a later maximum far above it restarts
+            m_run[nt] = m_run[nt] == -INFINITY ? mx : m_run[nt];
+            if (__any(mx > m_run[nt] + kSlack) && lane == 0) *restart_flag = 1;
+          }
+          const float m_use = (m_run[nt] == -INFINITY) ? 0.f : m_run[nt];
+          float ps = 0.f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            x[j] = __builtin_amdgcn_exp2f(x[j] - m_use);
+            ps += x[j];
+          }
+          l_run[nt] += ps;
+          pb[nt] = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                                    pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])});
         }
-        asm volatile("" ::: "memory");
       }
     }
+    if (pass == 0 && !restart) break;             // the common case: done in one pass
+    // drain this pass's copies before the tile buffers are refilled
+    vm_wait<0>();
+    block_sync_lds();
+    if (pass == 0) {
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) m_run[nt] = -INFINITY;
+    }
   }
+  if (!active) return;                            // no barrier follows
 
-  // ---- epilogue ----
-  float* const il = (float*)(lds_raw + C::OFF_IL);
-  if (smax_wave) {
-    const float lt = wave_sum_xor16_32(l_run);
-    if (q == 0) il[srow] = lt > 0.f ? 1.f / lt : 0.f;
-    if (q == 0 && svalid) {
-      const float lse_v = lt > 0.f ? (m_run + log2f(lt)) * kLn2 : -INFINITY;
-      const int h = srho / SQ, i = srho % SQ;
+  // ---- epilogue: lse, then out^T = W_UV^T o_lat^T straight from the accumulators ----
+  // The B operand of k step kk (latent block 32kk .. 32kk+31) for row c is
+  // lane (q, c): o_lat[16(2kk) + 4q + e] (e < 4) and o_lat[16(2kk+1) + 4q + e - 4]
+  // (e >= 4), i.e. the lane's own accumulators o[2kk] and o[2kk+1]; the
+  // workspace W_UV^T is stored with the latent index permuted the same way
+  // inside each 32-block, so the A operand is one 16-byte load.
+  const uint16_t* const wuvP = p.wuvT;
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    const float lt = wave_sum_q(l_run[nt]);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const int r_first = row0 + 16 * nt;
+    if (r_first >= rows_total) break;             // uniform
+    const int rho = r_first + c;
+    const bool valid = rho < rows_total;
+    const int h = valid ? rho / SQ : 0, i = valid ? rho % SQ : 0;
+    if (q == 0 && valid) {
+      const float lse_v = lt > 0.f ? (m_run[nt] + log2f(lt)) * kLn2 : -INFINITY;
       if (p.split_offsets) p.part_lse[((size_t)u * SQ + i) * H + h] = lse_v;
       else if (p.lse) p.lse[((size_t)b * SQ + i) * H + h] = lse_v;
     }
-  }
-  block_sync_lds();                               // 1/l ready; KV, S and P buffers free
-  // o_lat (normalised, bf16) -> LDS [row][R], 16-byte chunks swizzled by row
-  lds_u8_t* const olat = lds;
-  if (pv_active) {
+    const int r_last = min(r_first + 15, rows_total - 1);
+    const int g_lo = (r_first / SQ) / HPG, g_hi = (r_last / SQ) / HPG;
+    const int myG = valid ? h / HPG : -1;
+    // normalised o_lat of this row tile as bf16 B operands, built once
+    bf16x8 bo[R / 32];
 #pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) {
-      const int r = 16 * nt + c;
-      const float inv = il[r];
-#pragma unroll
-      for (int j = 0; j < MTW; ++j) {
-        const f32x4 v = o[j][nt] * inv;
-        const int ch = 2 * (mt0 + j) + (q >> 1);
-        const int pos = (ch & ~C::OSWZ) | ((ch ^ r) & C::OSWZ);
-        u32x2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        *(__attribute__((address_space(3))) u32x2*)(olat + (r * (R / 8) + pos) * 16 + (q & 1) * 8) = pk;
-      }
-    }
-  }
-  block_sync_lds();
-  // up-projection: wave w takes 16-row tile et = w / 2 and output dims
-  // [half * DV/2, (half + 1) * DV/2), half = w % 2:
-  // out^T[d][row] = sum_l W_UV^T[d][l] o_lat[row][l]
-  constexpr int MDH = MD >= 2 ? MD / 2 : 1;      // output tiles per wave
-  const int et = w >> 1, half = w & 1;
-  if (half * MDH >= MD) return;
-  const int erow = 16 * et + c;                   // block-local row of this lane
-  const int erho = row_base + erow;
-  const int r_first = row_base + 16 * et;
-  if (r_first >= rows_total) return;
-  const int r_last = min(r_first + 15, rows_total - 1);
-  const int g_lo = (r_first / SQ) / HPG, g_hi = (r_last / SQ) / HPG;
-  const bool evalid = erho < rows_total;
-  const int myG = evalid ? (erho / SQ) / HPG : -1;
-  for (int G = g_lo; G <= g_hi; ++G) {
-    const uint16_t* WT = p.wuvT + (size_t)G * DV * R;
-    f32x4 acc[MDH];
-#pragma unroll
-    for (int m = 0; m < MDH; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
     for (int kk = 0; kk < R / 32; ++kk) {
-      const int ch = 4 * kk + q;
-      const int pos = (ch & ~C::OSWZ) | ((ch ^ erow) & C::OSWZ);
-      const bf16x8 bo = __builtin_bit_cast(bf16x8, *(const lds_u32x4_t*)(olat + (erow * (R / 8) + pos) * 16));
-#pragma unroll
-      for (int m = 0; m < MDH; ++m) {
-        const int md = half * MDH + m;
-        acc[m] = mfma16(ld_bf16x8(WT + (size_t)(16 * md + c) * R + 32 * kk + 8 * q), bo, acc[m]);
-      }
+      const f32x4 lo4 = o[2 * kk][nt] * inv, hi4 = o[2 * kk + 1][nt] * inv;
+      bo[kk] = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(lo4[0], lo4[1]), pack_bf16x2(lo4[2], lo4[3]),
+                                                pack_bf16x2(hi4[0], hi4[1]), pack_bf16x2(hi4[2], hi4[3])});
     }
-    // acc[m] lane (q, c): dims 16md + 4q .. +3 of row erow
-    if (myG != G) continue;
-    const int h = erho / SQ, i = erho % SQ;
-    if (p.split_offsets) {
-      const size_t row = ((size_t)u * SQ + i) * H + h;
+    for (int G = g_lo; G <= g_hi; ++G) {
+      const uint16_t* WT = wuvP + (size_t)G * DV * R;
+      f32x4 acc[MD];
 #pragma unroll
-      for (int m = 0; m < MDH; ++m)
-        *reinterpret_cast<f32x4*>(p.part_out + row * DV + 16 * (half * MDH + m) + 4 * q) = acc[m];
-    } else {
-      const size_t row = ((size_t)b * SQ + i) * H + h;
+      for (int md = 0; md < MD; ++md) acc[md] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // W_UV^T operands loaded one k step ahead (the compiler barrier keeps
+      // the remaining loads from being hoisted into a register flood)
+      bf16x8 wa[2][MD];
 #pragma unroll
-      for (int m = 0; m < MDH; ++m) {
-        u32x2 pk = {pack_bf16x2(acc[m][0], acc[m][1]), pack_bf16x2(acc[m][2], acc[m][3])};
-        *reinterpret_cast<u32x2*>(p.out + row * DV + 16 * (half * MDH + m) + 4 * q) = pk;
+      for (int md = 0; md < MD; ++md) wa[0][md] = ld_bf16x8(WT + (size_t)(16 * md + c) * R + 8 * q);
+#pragma unroll
+      for (int kk = 0; kk < R / 32; ++kk) {
+        if (kk + 1 < R / 32) {
+#pragma unroll
+          for (int md = 0; md < MD; ++md)
+            wa[(kk + 1) & 1][md] = ld_bf16x8(WT + (size_t)(16 * md + c) * R + 32 * (kk + 1) + 8 * q);
+        }
+#pragma unroll
+        for (int md = 0; md < MD; ++md) acc[md] = mfma16(wa[kk & 1][md], bo[kk], acc[md]);
+        asm volatile("" ::: "memory");
+      }
+      // acc[md] lane (q, c): output dims 16md + 4q .. +3 of row c
+      if (myG != G) continue;
+      if (p.split_offsets) {
+        const size_t row = ((size_t)u * SQ + i) * H + h;
+#pragma unroll
+        for (int md = 0; md < MD; ++md)
+          *reinterpret_cast<f32x4*>(p.part_out + row * DV + 16 * md + 4 * q) = acc[md];
+      } else {
+        const size_t row = ((size_t)b * SQ + i) * H + h;
+#pragma unroll
+        for (int md = 0; md < MD; ++md) {
+          u32x2 pk = {pack_bf16x2(acc[md][0], acc[md][1]), pack_bf16x2(acc[md][2], acc[md][3])};
+          *reinterpret_cast<u32x2*>(p.out + row * DV + 16 * md + 4 * q) = pk;
+        }
       }
     }
   }
@@ -492,19 +553,24 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(DecodeParams p) {
   }
 }
 
-// W_UV[G] (r x d_v) -> W_UV^T[G] (d_v x r), so the up-projection operand (8
-// consecutive latent rows of one output column) is one contiguous load.
+// W_UV[G] (r x d_v) -> W_UV^T[G] (d_v x r) with the latent index permuted
+// inside each 32-wide block: position 8q + e holds latent 4q + e (e < 4) or
+// 16 + 4q + e - 4 (e >= 4), the order in which lane q of the decode kernel's
+// accumulators holds o_lat, so the up-projection's A operand (8 positions of
+// one output column) is one contiguous 16-byte load.
 template <int R, int DV>
 __global__ __launch_bounds__(256) void wuv_transpose_kernel(DecodeParams p) {
   const int G = blockIdx.y;
   const int idx = blockIdx.x * 256 + threadIdx.x;     // one latent row x 8 columns
   if (idx >= R * (DV / 8)) return;
   const int l = idx / (DV / 8), d0 = (idx % (DV / 8)) * 8;
+  const int lb = l & 31;
+  const int pos = (l & ~31) | (8 * ((lb & 15) >> 2) + 4 * (lb >> 4) + (lb & 3));
   const u32x4 v = *reinterpret_cast<const u32x4*>(p.w_uv + ((size_t)G * R + l) * DV + d0);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const uint16_t e = (uint16_t)(v[j / 2] >> (16 * (j & 1)));
-    p.wuvT[((size_t)G * DV + d0 + j) * R + l] = e;
+    p.wuvT[((size_t)G * DV + d0 + j) * R + pos] = e;
   }
 }
 
@@ -528,7 +594,7 @@ hipError_t launch_absorb(const DecodeParams& p, hipStream_t stream) {
   const int rows_total = HPG * p.num_groups * SQ;
   const int RB = (rows_total + C::ROWS_WG - 1) / C::ROWS_WG;
   const unsigned grid = (unsigned)((p.num_units + 7) / 8) * 8u * (unsigned)RB;
-  hipLaunchKernelGGL((absorb_decode_kernel<HPG, SQ, R, DR, DN, DV>), dim3(grid), dim3(512), 0,
+  hipLaunchKernelGGL((absorb_decode_kernel<HPG, SQ, R, DR, DN, DV>), dim3(grid), dim3(64 * C::NW), 0,
                      stream, p);
   return hipGetLastError();
 }

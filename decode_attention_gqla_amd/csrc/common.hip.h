@@ -80,6 +80,41 @@ __device__ __forceinline__ float wave_sum_xor16_32(float v) {
   return v;
 }
 
+// Max / sum over the four lanes c, c+16, c+32, c+48 (the 4 lane groups q
+// holding one MFMA column), with the gfx950 cross-lane swaps instead of an
+// LDS permute: v_permlane16_swap a, b (a and b both holding x) leaves
+// {x of lane l, x of lane l ^ 16} in {a, b} on every lane (likewise
+// v_permlane32_swap with l ^ 32).  Written as asm on two distinct registers:
+// the compiler's model of the builtin with equal inputs folds the two
+// results into one.  The s_nops cover the VALU -> permlane -> VALU hazards
+// the compiler cannot see inside asm.
+__device__ __forceinline__ void swap_pairs16(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap_pairs32(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+
+__device__ __forceinline__ float wave_max_q(float v) {
+  float a = v, b = v;
+  swap_pairs16(a, b);
+  v = fmaxf(a, b);
+  a = v;
+  b = v;
+  swap_pairs32(a, b);
+  return fmaxf(a, b);
+}
+
+__device__ __forceinline__ float wave_sum_q(float v) {
+  float a = v, b = v;
+  swap_pairs16(a, b);
+  v = a + b;
+  a = v;
+  b = v;
+  swap_pairs32(a, b);
+  return a + b;
+}
+
 typedef __attribute__((address_space(3))) unsigned char lds_u8_t;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4_t;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
@@ -93,8 +128,9 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 // the same asm block; the one wait state between the M0 write and the copy is
 // the s_nop.  There are no register outputs.
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff_bytes, lds_u8_t* lds_base) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff_bytes), "s"(base), "s"((uint32_t)(uintptr_t)lds_base) : "memory", "m0");
+               :: "v"(voff_bytes), "s"(base), "s"(m0v) : "memory", "m0");
 }
 
 // s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
