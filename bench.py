@@ -152,11 +152,9 @@ def main():
     lse_a = torch.empty(B, 1, 128, dtype=torch.float32, device=dev)
     out_g = torch.empty(B, 2, 128, 128, dtype=torch.bfloat16, device=dev)
     lse_g = torch.empty(B, 2, 128, dtype=torch.float32, device=dev)
-    ws = G.absorb_workspace(d1, B)
     sa = G.make_split_plan(lens, args.absorb_split) + (args.absorb_split,) if args.absorb_split else None
     sg = G.make_split_plan(lens, args.gqa_split) + (args.gqa_split,) if args.gqa_split else None
-    pa = (torch.empty(sa[1], 1, 128, 128, dtype=torch.float32, device=dev),
-          torch.empty(sa[1], 1, 128, dtype=torch.float32, device=dev)) if sa else (None, None)
+    ws = G.absorb_workspace(d1, B, total_splits=sa[1] if sa else 0)
     pg = (torch.empty(sg[1], 2, 128, 128, dtype=torch.float32, device=dev),
           torch.empty(sg[1], 2, 128, dtype=torch.float32, device=dev)) if sg else (None, None)
 
@@ -164,7 +162,7 @@ def main():
         G.gqla_decode_mqa_absorb(d1, qa_n, qa_r, pages, bt, sl, w_uk, w_uv, out=out_a, lse=lse_a,
                                  split_offsets=sa[0] if sa else None,
                                  split_tokens=sa[2] if sa else 0, total_splits=sa[1] if sa else 0,
-                                 part_out=pa[0], part_lse=pa[1], workspace=ws)
+                                 workspace=ws)
 
     def run_gqa():
         G.gqla_decode_gqa(d2, qg_n, qg_r, E, bt, sl, out=out_g, lse=lse_g,

@@ -19,7 +19,7 @@ __all__ = [
     "GqlaError", "Dims", "lib", "gqla_expand_cache", "gqla_decode_mqa_absorb", "gqla_decode_gqa",
     "gqla_splitkv_combine", "gqla_status_string", "make_split_plan", "latent_page_elems",
     "expanded_page_elems", "decode_mqa_absorb", "decode_gqa", "expand_cache",
-    "gqla_mqa_absorb_workspace_bytes", "absorb_workspace",
+    "gqla_mqa_absorb_workspace_bytes", "gqla_mqa_absorb_workspace_offsets", "absorb_workspace",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -63,9 +63,12 @@ _SIGS = {
                            ctypes.c_int64, _vp, _vp], ctypes.c_int),
     "gqla_decode_mqa_absorb": ([ctypes.POINTER(Dims), ctypes.c_int32, _vp, _vp, _vp, _i32p,
                                 ctypes.c_int32, _i32p, _vp, _vp, _i32p, ctypes.c_int32,
-                                ctypes.c_int32, _vp, _f32p, _f32p, _f32p, _vp, ctypes.c_uint64,
-                                _vp], ctypes.c_int),
-    "gqla_mqa_absorb_workspace_bytes": ([ctypes.POINTER(Dims), ctypes.c_int32], ctypes.c_uint64),
+                                ctypes.c_int32, _vp, _f32p, _vp, ctypes.c_uint64, _vp],
+                               ctypes.c_int),
+    "gqla_mqa_absorb_workspace_bytes": ([ctypes.POINTER(Dims), ctypes.c_int32, ctypes.c_int32],
+                                        ctypes.c_uint64),
+    "gqla_mqa_absorb_workspace_offsets": ([ctypes.POINTER(Dims), ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.POINTER(ctypes.c_uint64)], ctypes.c_int),
     "gqla_decode_gqa": ([ctypes.POINTER(Dims), ctypes.c_int32, _vp, _vp, _vp, _i32p,
                          ctypes.c_int32, _i32p, _i32p, ctypes.c_int32, ctypes.c_int32, _vp,
                          _f32p, _f32p, _f32p, _vp], ctypes.c_int),
@@ -175,16 +178,24 @@ def _decode_common(d, q_nope, q_rope, block_table, cache_seqlens, split_offsets,
     return B, block_table.shape[1], args
 
 
-def gqla_mqa_absorb_workspace_bytes(d: Dims, batch: int) -> int:
-    return int(lib().gqla_mqa_absorb_workspace_bytes(ctypes.byref(d), int(batch)))
+def gqla_mqa_absorb_workspace_bytes(d: Dims, batch: int, total_splits: int = 0) -> int:
+    return int(lib().gqla_mqa_absorb_workspace_bytes(ctypes.byref(d), int(batch),
+                                                      int(total_splits)))
+
+
+def gqla_mqa_absorb_workspace_offsets(d: Dims, batch: int, total_splits: int = 0) -> list[int]:
+    """Byte offsets of the absorb workspace regions: q_abs rows, W_UV^T, split o_lat, split lse."""
+    off = (ctypes.c_uint64 * 4)()
+    _check(lib().gqla_mqa_absorb_workspace_offsets(ctypes.byref(d), int(batch), int(total_splits),
+                                                   off), "gqla_mqa_absorb_workspace_offsets")
+    return [int(x) for x in off]
 
 
 def gqla_decode_mqa_absorb(d: Dims, q_nope, q_rope, latent_pages, block_table, cache_seqlens,
                            w_uk, w_uv, out=None, lse=None, split_offsets=None, split_tokens=0,
-                           total_splits=0, part_out=None, part_lse=None, workspace=None,
-                           stream=None) -> None:
+                           total_splits=0, workspace=None, stream=None) -> None:
     B, mb, a = _decode_common(d, q_nope, q_rope, block_table, cache_seqlens, split_offsets,
-                              total_splits, out, lse, part_out, part_lse)
+                              total_splits, out, lse, None, None)
     if workspace is None:
         raise ValueError("workspace is required (see gqla_mqa_absorb_workspace_bytes)")
     ws = _ptr(workspace, torch.uint8, "workspace")
@@ -194,7 +205,7 @@ def gqla_decode_mqa_absorb(d: Dims, q_nope, q_rope, latent_pages, block_table, c
         _ptr(w_uk, torch.bfloat16, "w_uk", (d.num_groups, d.d_latent, d.d_nope)),
         _ptr(w_uv, torch.bfloat16, "w_uv", (d.num_groups, d.d_latent, d.d_v)),
         a["split_offsets"], int(split_tokens), int(total_splits), a["out"], a["lse"],
-        a["part_out"], a["part_lse"], ws, int(workspace.numel()), _stream(stream))
+        ws, int(workspace.numel()), _stream(stream))
     _check(st, "gqla_decode_mqa_absorb")
 
 
@@ -248,9 +259,9 @@ def _partials(d, total, device):
             torch.empty(total, d.s_q, d.num_heads, dtype=torch.float32, device=device))
 
 
-def absorb_workspace(d: Dims, batch: int, device="cuda"):
+def absorb_workspace(d: Dims, batch: int, device="cuda", total_splits: int = 0):
     """A workspace tensor (uint8) large enough for gqla_decode_mqa_absorb."""
-    n = gqla_mqa_absorb_workspace_bytes(d, batch)
+    n = gqla_mqa_absorb_workspace_bytes(d, batch, total_splits)
     return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
 
 
@@ -259,17 +270,16 @@ def decode_mqa_absorb(d: Dims, q_nope, q_rope, latent_pages, block_table, cache_
     """Allocate outputs and run the absorb path; ``split`` = (split_offsets, total, split_tokens)."""
     B = q_nope.shape[0]
     out, lse = _outputs(d, B, q_nope.device, with_lse)
-    ws = workspace if workspace is not None else absorb_workspace(d, B, q_nope.device)
+    total = split[1] if split is not None else 0
+    ws = workspace if workspace is not None else absorb_workspace(d, B, q_nope.device, total)
     if split is None:
         gqla_decode_mqa_absorb(d, q_nope, q_rope, latent_pages, block_table, cache_seqlens, w_uk,
                                w_uv, out=out, lse=lse, workspace=ws, stream=stream)
     else:
         offs, total, tokens = split
-        po, pl = _partials(d, total, q_nope.device)
         gqla_decode_mqa_absorb(d, q_nope, q_rope, latent_pages, block_table, cache_seqlens, w_uk,
                                w_uv, out=out, lse=lse, split_offsets=offs, split_tokens=tokens,
-                               total_splits=total, part_out=po, part_lse=pl, workspace=ws,
-                               stream=stream)
+                               total_splits=total, workspace=ws, stream=stream)
     return out, lse
 
 

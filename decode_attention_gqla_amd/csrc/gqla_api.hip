@@ -49,12 +49,14 @@ float scale_of(const gqla_dims* d) {
 }
 
 // Shared checks of the two decode entry points.  cache/w_uk/w_uv are checked
-// by the caller (the GQA path has no weights).
+// by the caller (the GQA path has no weights).  `partials`: the split plan
+// writes caller-provided part_out / part_lse (GQA path); otherwise `out` is
+// always required (the absorb path merges its splits itself).
 int check_decode(const gqla_dims* d, int32_t batch, const void* q_nope, const void* q_rope,
                  const void* cache, const int32_t* block_table, int32_t max_blocks,
                  const int32_t* seqlens, const int32_t* split_offsets, int32_t split_tokens,
                  int32_t total_splits, const void* out, const float* lse, const float* part_out,
-                 const float* part_lse) {
+                 const float* part_lse, bool partials) {
   int st = check_dims(d);
   if (st != GQLA_OK) return st;
   if (batch < 0 || max_blocks <= 0) return GQLA_ERR_INVALID_ARG;
@@ -66,8 +68,12 @@ int check_decode(const gqla_dims* d, int32_t batch, const void* q_nope, const vo
     if (split_tokens <= 0 || split_tokens % d->block_size != 0 || total_splits < batch)
       return GQLA_ERR_BAD_SPLIT_PLAN;
     if (!aligned4(split_offsets)) return GQLA_ERR_MISALIGNED;
-    if (!part_out || !part_lse) return GQLA_ERR_INVALID_ARG;
-    if (!aligned16(part_out) || !aligned4(part_lse)) return GQLA_ERR_MISALIGNED;
+    if (partials) {
+      if (!part_out || !part_lse) return GQLA_ERR_INVALID_ARG;
+      if (!aligned16(part_out) || !aligned4(part_lse)) return GQLA_ERR_MISALIGNED;
+    } else if (!out) {
+      return GQLA_ERR_INVALID_ARG;
+    }
   } else {
     if (!out) return GQLA_ERR_INVALID_ARG;
   }
@@ -103,6 +109,8 @@ gqla::DecodeParams make_params(const gqla_dims* d, int32_t batch, const void* q_
   p.scale_log2 = scale_of(d) * gqla::kLog2e;
   p.qcat = nullptr;
   p.wuvT = nullptr;
+  p.olat = nullptr;
+  p.olse = nullptr;
   return p;
 }
 
@@ -131,7 +139,7 @@ int enqueue_combine(const gqla_dims* d, int32_t batch, const int32_t* split_offs
 
 extern "C" {
 
-int gqla_abi_version(void) { return 100; }
+int gqla_abi_version(void) { return 200; }
 
 const char* gqla_status_string(int status) {
   switch (status) {
@@ -155,18 +163,41 @@ int64_t gqla_expanded_page_elems(const gqla_dims* d) {
   return (int64_t)d->block_size * ((int64_t)d->num_groups * (d->d_nope + d->d_v) + d->d_rope);
 }
 
-// Workspace of the absorb path: the absorbed queries [batch][s_q][h_q][r + d_rope]
-// (bf16), then (256-byte aligned) W_UV transposed, [g][d_v][r] (bf16).
-static uint64_t absorb_q_bytes(const gqla_dims* d, int32_t batch) {
-  const uint64_t n = (uint64_t)batch * d->s_q * d->num_heads * (uint64_t)(d->d_latent + d->d_rope) * 2u;
-  return (n + 255u) & ~(uint64_t)255u;
+// Workspace of the absorb path, four regions each starting on a 256-byte
+// boundary: the absorbed query rows [batch][s_q][h_q][r + d_rope] (bf16),
+// W_UV transposed [g][d_v][r] (bf16), the split partials o_lat
+// [units][s_q][h_q][r] (bf16) and their lse [units][s_q][h_q] (fp32), with
+// units = total_splits under a split plan, else batch.
+static bool absorb_ws_dims_ok(const gqla_dims* d, int32_t batch, int32_t total_splits) {
+  return d && batch > 0 && total_splits >= 0 && d->s_q > 0 && d->num_heads > 0 && d->d_latent > 0 &&
+         d->d_rope >= 0 && d->num_groups > 0 && d->d_v > 0;
 }
 
-uint64_t gqla_mqa_absorb_workspace_bytes(const gqla_dims* d, int32_t batch) {
-  if (!d || batch <= 0 || d->s_q <= 0 || d->num_heads <= 0 || d->d_latent <= 0 || d->d_rope < 0 ||
-      d->num_groups <= 0 || d->d_v <= 0)
-    return 0;
-  return absorb_q_bytes(d, batch) + (uint64_t)d->num_groups * d->d_v * (uint64_t)d->d_latent * 2u;
+static void absorb_ws_layout(const gqla_dims* d, int32_t batch, int32_t total_splits, uint64_t off[5]) {
+  auto up = [](uint64_t n) { return (n + 255u) & ~(uint64_t)255u; };
+  const uint64_t rows = (uint64_t)d->s_q * d->num_heads;
+  const uint64_t units = total_splits > 0 ? (uint64_t)total_splits : (uint64_t)batch;
+  off[0] = 0;
+  off[1] = off[0] + up((uint64_t)batch * rows * (uint64_t)(d->d_latent + d->d_rope) * 2u);
+  off[2] = off[1] + up((uint64_t)d->num_groups * d->d_v * (uint64_t)d->d_latent * 2u);
+  off[3] = off[2] + up(units * rows * (uint64_t)d->d_latent * 2u);
+  off[4] = off[3] + up(units * rows * 4u);
+}
+
+uint64_t gqla_mqa_absorb_workspace_bytes(const gqla_dims* d, int32_t batch, int32_t total_splits) {
+  if (!absorb_ws_dims_ok(d, batch, total_splits)) return 0;
+  uint64_t off[5];
+  absorb_ws_layout(d, batch, total_splits, off);
+  return off[4];
+}
+
+int gqla_mqa_absorb_workspace_offsets(const gqla_dims* d, int32_t batch, int32_t total_splits,
+                                      uint64_t* offsets) {
+  if (!absorb_ws_dims_ok(d, batch, total_splits) || !offsets) return GQLA_ERR_INVALID_ARG;
+  uint64_t off[5];
+  absorb_ws_layout(d, batch, total_splits, off);
+  for (int i = 0; i < 4; ++i) offsets[i] = off[i];
+  return GQLA_OK;
 }
 
 int gqla_expand_cache(const gqla_dims* d, const void* latent_pages, const void* w_uk,
@@ -200,30 +231,32 @@ int gqla_decode_mqa_absorb(const gqla_dims* d, int32_t batch, const void* q_nope
                            const int32_t* block_table, int32_t max_blocks,
                            const int32_t* cache_seqlens, const void* w_uk, const void* w_uv,
                            const int32_t* split_offsets, int32_t split_tokens,
-                           int32_t total_splits, void* out, float* lse, float* part_out,
-                           float* part_lse, void* workspace, uint64_t workspace_bytes,
-                           void* stream) {
+                           int32_t total_splits, void* out, float* lse, void* workspace,
+                           uint64_t workspace_bytes, void* stream) {
   int st = check_decode(d, batch, q_nope, q_rope, latent_pages, block_table, max_blocks,
                         cache_seqlens, split_offsets, split_tokens, total_splits, out, lse,
-                        part_out, part_lse);
+                        nullptr, nullptr, false);
   if (st != GQLA_OK) return st;
   if (!w_uk || !w_uv) return GQLA_ERR_INVALID_ARG;
   if (!aligned16(w_uk) || !aligned16(w_uv)) return GQLA_ERR_MISALIGNED;
   if (batch == 0) return GQLA_OK;
-  if (!workspace || workspace_bytes < gqla_mqa_absorb_workspace_bytes(d, batch))
+  const int32_t ws_splits = split_offsets ? total_splits : 0;
+  if (!workspace || workspace_bytes < gqla_mqa_absorb_workspace_bytes(d, batch, ws_splits))
     return GQLA_ERR_INVALID_ARG;
   if (!aligned16(workspace)) return GQLA_ERR_MISALIGNED;
   gqla::DecodeParams p = make_params(d, batch, q_nope, q_rope, latent_pages, block_table,
                                      max_blocks, cache_seqlens, w_uk, w_uv, split_offsets,
-                                     split_tokens, total_splits, out, lse, part_out, part_lse);
-  p.qcat = (uint16_t*)workspace;
-  p.wuvT = (uint16_t*)((char*)workspace + absorb_q_bytes(d, batch));
+                                     split_tokens, total_splits, out, lse, nullptr, nullptr);
+  uint64_t off[5];
+  absorb_ws_layout(d, batch, ws_splits, off);
+  p.qcat = (uint16_t*)((char*)workspace + off[0]);
+  p.wuvT = (uint16_t*)((char*)workspace + off[1]);
+  p.olat = (uint16_t*)((char*)workspace + off[2]);
+  p.olse = (float*)((char*)workspace + off[3]);
   bool ok = true;
   hipError_t e = gqla::absorb_dispatch(d->num_heads / d->num_groups, d->s_q, d->d_latent,
                                        d->d_nope, d->d_v, d->d_rope, p, (hipStream_t)stream, &ok);
-  st = finish(e, ok);
-  if (st != GQLA_OK || !split_offsets || !out) return st;
-  return enqueue_combine(d, batch, split_offsets, part_out, part_lse, out, lse, (hipStream_t)stream);
+  return finish(e, ok);
 }
 
 int gqla_decode_gqa(const gqla_dims* d, int32_t batch, const void* q_nope, const void* q_rope,
@@ -233,7 +266,7 @@ int gqla_decode_gqa(const gqla_dims* d, int32_t batch, const void* q_nope, const
                     float* part_out, float* part_lse, void* stream) {
   int st = check_decode(d, batch, q_nope, q_rope, expanded_pages, block_table, max_blocks,
                         cache_seqlens, split_offsets, split_tokens, total_splits, out, lse,
-                        part_out, part_lse);
+                        part_out, part_lse, true);
   if (st != GQLA_OK) return st;
   if (batch == 0) return GQLA_OK;
   gqla::DecodeParams p = make_params(d, batch, q_nope, q_rope, expanded_pages, block_table,

@@ -15,6 +15,8 @@ struct DecodeParams {
   const int32_t* split_offsets;  // [B+1] or nullptr
   uint16_t* qcat;                // absorb path: [B][s_q][h_q][r + d_rope] workspace
   uint16_t* wuvT;                // absorb path: [g][d_v][r] workspace (W_UV transposed)
+  uint16_t* olat;                // absorb path: [units][s_q][h_q][r] workspace (split o_lat, bf16)
+  float* olse;                   // absorb path: [units][s_q][h_q] workspace (split lse)
   uint16_t* out;                 // [B][s_q][h_q][d_v] bf16 (unsplit launch)
   float* lse;                    // [B][s_q][h_q] or nullptr (unsplit launch)
   float* part_out;               // [S][s_q][h_q][d_v] (split launch)

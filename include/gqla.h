@@ -122,37 +122,58 @@ int gqla_expand_cache(const gqla_dims* d, const void* latent_pages, const void* 
  *   q_nope  bf16 [batch][s_q][h_q][d_nope]     q_rope bf16 [batch][s_q][h_q][d_rope]
  *   latent_pages as for gqla_expand_cache; block_table int32 [batch][max_blocks];
  *   cache_seqlens int32 [batch]; w_uk, w_uv as for gqla_expand_cache.
- *   split_offsets   NULL => one split per sequence (no partials touched), else the
- *                   split plan described above.
- *   out      bf16 [batch][s_q][h_q][d_v] or NULL.  With a split plan and out != NULL
- *            the merge (gqla_splitkv_combine) is enqueued after the decode.
+ *   split_offsets   NULL => one split per sequence, else the split plan
+ *                   described above.
+ *   out      bf16 [batch][s_q][h_q][d_v], required in both modes.
  *   lse      fp32 [batch][s_q][h_q] or NULL.
- *   part_out fp32 [total_splits][s_q][h_q][d_v], part_lse fp32 [total_splits][s_q][h_q]:
- *            required iff split_offsets != NULL.  W_UV[G] is applied per split
- *            (exact by linearity), so partials are in the output space.
- *   workspace  device scratch of at least gqla_mqa_absorb_workspace_bytes(d, batch)
- *            bytes, 16-byte aligned, owned by the caller; it receives the
- *            absorbed queries [batch][s_q][h_q][d_latent + d_rope] (bf16) and a
- *            transposed copy of W_UV, and must not be shared by calls that may
- *            run concurrently.  Too small or NULL returns GQLA_ERR_INVALID_ARG. */
+ *   workspace  device scratch of at least
+ *            gqla_mqa_absorb_workspace_bytes(d, batch, split_offsets ? total_splits : 0)
+ *            bytes, 16-byte aligned, owned by the caller; it must not be shared
+ *            by calls that may run concurrently.  Too small or NULL returns
+ *            GQLA_ERR_INVALID_ARG.  Its four regions (byte offsets from
+ *            gqla_mqa_absorb_workspace_offsets) hold, after the call:
+ *              [0] the absorbed query rows q_abs ++ q_rope, bf16
+ *                  [batch][s_q][h_q][d_latent + d_rope];
+ *              [1] W_UV transposed, bf16 [g][d_v][d_latent];
+ *              [2] the per-split normalised latent outputs o_lat, bf16
+ *                  [units][s_q][h_q][d_latent] (units = total_splits under a
+ *                  split plan, else batch with unit b = sequence b);
+ *              [3] their lse, fp32 [units][s_q][h_q] (-inf and o_lat = 0 for a
+ *                  row that sees no token of the split).
+ * The splits are merged in the latent space (log-sum-exp weights, fp32) and
+ * the merged o_lat is up-projected once per row; by linearity this equals
+ * merging per-split up-projected outputs.  No part_out / part_lse buffers. */
 int gqla_decode_mqa_absorb(const gqla_dims* d, int32_t batch, const void* q_nope,
                            const void* q_rope, const void* latent_pages,
                            const int32_t* block_table, int32_t max_blocks,
                            const int32_t* cache_seqlens, const void* w_uk, const void* w_uv,
                            const int32_t* split_offsets, int32_t split_tokens,
-                           int32_t total_splits, void* out, float* lse, float* part_out,
-                           float* part_lse, void* workspace, uint64_t workspace_bytes,
-                           void* stream);
+                           int32_t total_splits, void* out, float* lse, void* workspace,
+                           uint64_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace gqla_decode_mqa_absorb needs for `batch` sequences
- * (0 for batch <= 0 or d == NULL). */
-uint64_t gqla_mqa_absorb_workspace_bytes(const gqla_dims* d, int32_t batch);
+ * and `total_splits` splits (0 = no split plan); 0 for batch <= 0,
+ * total_splits < 0 or d == NULL. */
+uint64_t gqla_mqa_absorb_workspace_bytes(const gqla_dims* d, int32_t batch, int32_t total_splits);
+
+/* Byte offsets of the four workspace regions listed above (offsets[0..3]);
+ * GQLA_ERR_INVALID_ARG for the arguments gqla_mqa_absorb_workspace_bytes
+ * answers 0 for, or offsets == NULL. */
+int gqla_mqa_absorb_workspace_offsets(const gqla_dims* d, int32_t batch, int32_t total_splits,
+                                      uint64_t* offsets);
 
 /* GQA decode over the per-group expanded cache (paperlayer.ai section 4,
  * "GQA path"; gist.science section 2 "GQA-Pfad": conventional grouped-query
  * attention with no per-step latent expansion).  Arguments as for
  * gqla_decode_mqa_absorb, with expanded_pages (bf16 [num_pages]
- * [gqla_expanded_page_elems]) in place of the latent cache and no weights. */
+ * [gqla_expanded_page_elems]) in place of the latent cache, no weights and no
+ * workspace, and:
+ *   out      bf16 [batch][s_q][h_q][d_v]: required without a split plan; with
+ *            one and out != NULL, gqla_splitkv_combine is enqueued after the
+ *            decode.
+ *   part_out fp32 [total_splits][s_q][h_q][d_v], part_lse fp32
+ *            [total_splits][s_q][h_q]: the per-split partials, required iff
+ *            split_offsets != NULL. */
 int gqla_decode_gqa(const gqla_dims* d, int32_t batch, const void* q_nope, const void* q_rope,
                     const void* expanded_pages, const int32_t* block_table, int32_t max_blocks,
                     const int32_t* cache_seqlens, const int32_t* split_offsets,

@@ -309,6 +309,45 @@ def decode_partials(q_nope, q_rope, pages, block_table, seqlens, w_uk, w_uv, d: 
     return np.stack(parts_o), np.stack(parts_l), np.array(offsets)
 
 
+def decode_partials_latent(q_nope, q_rope, pages, block_table, seqlens, w_uk, d: Dims,
+                           split_tokens: int):
+    """Per-split normalized latent outputs and lse, absorb form.
+
+    For split [lo, hi) of sequence b and row (i, h) of group G:
+    q_abs = W_UK[G] q_nope[b,i,h], s_t = (q_abs . c_t + q_rope . k_rope_t) * scale
+    over the visible tokens t in [lo, hi), o_lat = softmax(s) C (d_latent wide).
+    These are the split partials of the MQA-absorb path taken before the
+    up-projection by W_UV[G] (paperlayer.ai section 4, "MQA-absorb path":
+    attention runs over the latent, W_UV maps its output back); o_lat W_UV[G]
+    is the ``decode_partials`` output of the same split, by linearity.
+    A split with no visible token has o_lat = 0 and lse = -inf.
+    Returns (part_lat [S, s_q, h_q, d_latent], part_lse [S, s_q, h_q], offsets [B+1]).
+    """
+    q_nope, q_rope, w_uk = map(_f64, (q_nope, q_rope, w_uk))
+    B = q_nope.shape[0]
+    parts_o, parts_l, offsets = [], [], [0]
+    for b in range(B):
+        L = int(seqlens[b])
+        C, KR = gather_latent(pages, block_table[b], L, d)
+        ranges = split_ranges(L, split_tokens)
+        offsets.append(offsets[-1] + len(ranges))
+        for lo, hi in ranges:
+            po = np.zeros((d.s_q, d.h_q, d.r))
+            pl = np.full((d.s_q, d.h_q), -np.inf)
+            for h in range(d.h_q):
+                G = h // d.heads_per_group
+                for i in range(d.s_q):
+                    n_hi = min(hi, visible_tokens(L, i, d.s_q))
+                    if n_hi <= lo:
+                        continue
+                    q_abs = w_uk[G] @ q_nope[b, i, h]
+                    s = (C[lo:n_hi] @ q_abs + KR[lo:n_hi] @ q_rope[b, i, h]) * d.scale
+                    po[i, h], pl[i, h] = _softmax_attend(s, C[lo:n_hi])
+            parts_o.append(po)
+            parts_l.append(pl)
+    return np.stack(parts_o), np.stack(parts_l), np.array(offsets)
+
+
 def combine(part_out, part_lse, split_offsets):
     """Merge normalized split partials by log-sum-exp.
 

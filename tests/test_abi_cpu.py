@@ -55,9 +55,10 @@ def dsv3(s_q=1, **kw):
 
 def absorb(lib, d, batch=1, q=A, split=None, split_tokens=0, total=0, out=A, part=(None, None),
            ws=A, ws_bytes=1 << 40):
+    # the absorb path has no partial buffers (it merges its splits itself)
     return lib.gqla_decode_mqa_absorb(ctypes.byref(d) if d is not None else None, batch, q, A, A,
                                       A, 4, A, A, A, split, split_tokens, total, out, None,
-                                      part[0], part[1], ws, ws_bytes, None)
+                                      ws, ws_bytes, None)
 
 
 def gqa(lib, d, batch=1, q=A, split=None, split_tokens=0, total=0, out=A, part=(None, None)):
@@ -98,7 +99,11 @@ def test_decode_argument_errors_return_before_any_launch(lib, call):
     assert call(lib, dsv3(), split=A, split_tokens=100, total=4, part=(A, B_)) == BADSPLIT
     assert call(lib, dsv3(), split=A, split_tokens=0, total=4, part=(A, B_)) == BADSPLIT
     assert call(lib, dsv3(), batch=4, split=A, split_tokens=1024, total=2, part=(A, B_)) == BADSPLIT
-    assert call(lib, dsv3(), split=A, split_tokens=1024, total=4, part=(None, B_)) == INVALID
+    if call is gqa:   # the GQA split plan writes caller partials
+        assert call(lib, dsv3(), split=A, split_tokens=1024, total=4, part=(None, B_)) == INVALID
+        assert call(lib, dsv3(), split=A, split_tokens=1024, total=4, part=(ODD, B_)) == MISALIGNED
+    else:             # the absorb path always writes out
+        assert call(lib, dsv3(), split=A, split_tokens=1024, total=4, out=None) == INVALID
     # an empty batch is a valid no-op
     assert call(lib, dsv3(), batch=0) == OK
     assert call(lib, dsv3(), batch=0, split=A, split_tokens=1024, total=0, part=(A, B_)) == OK
@@ -107,14 +112,27 @@ def test_decode_argument_errors_return_before_any_launch(lib, call):
 def test_absorb_needs_weights_and_workspace(lib):
     d = dsv3()
     st = lib.gqla_decode_mqa_absorb(ctypes.byref(d), 1, A, A, A, A, 4, A, None, A, None, 0, 0, A,
-                                    None, None, None, A, 1 << 40, None)
+                                    None, A, 1 << 40, None)
     assert st == INVALID
-    need = lib.gqla_mqa_absorb_workspace_bytes(ctypes.byref(d), 3)
-    assert need == 3 * 1 * 128 * 576 * 2 + 8 * 128 * 512 * 2
+    up = lambda n: (n + 255) // 256 * 256
+    rows = 1 * 128
+    # q_abs rows, W_UV^T, split o_lat (bf16) and split lse (fp32); units = batch unsplit
+    need = lib.gqla_mqa_absorb_workspace_bytes(ctypes.byref(d), 3, 0)
+    assert need == up(3 * rows * 576 * 2) + up(8 * 128 * 512 * 2) + up(3 * rows * 512 * 2) + up(3 * rows * 4)
+    need7 = lib.gqla_mqa_absorb_workspace_bytes(ctypes.byref(d), 3, 7)
+    assert need7 == up(3 * rows * 576 * 2) + up(8 * 128 * 512 * 2) + up(7 * rows * 512 * 2) + up(7 * rows * 4)
+    off = (ctypes.c_uint64 * 4)()
+    assert lib.gqla_mqa_absorb_workspace_offsets(ctypes.byref(d), 3, 7, off) == OK
+    assert list(off) == [0, up(3 * rows * 576 * 2), up(3 * rows * 576 * 2) + up(8 * 128 * 512 * 2),
+                         up(3 * rows * 576 * 2) + up(8 * 128 * 512 * 2) + up(7 * rows * 512 * 2)]
+    assert lib.gqla_mqa_absorb_workspace_offsets(ctypes.byref(d), 0, 7, off) == INVALID
     assert absorb(lib, d, batch=3, ws_bytes=need - 1) == INVALID
     assert absorb(lib, d, batch=3, ws=None, ws_bytes=need) == INVALID
     assert absorb(lib, d, batch=3, ws=ODD, ws_bytes=need) == MISALIGNED
-    assert lib.gqla_mqa_absorb_workspace_bytes(None, 3) == 0
+    # a split plan needs room for its partials
+    assert absorb(lib, d, batch=3, split=A, split_tokens=1024, total=7, ws_bytes=need7 - 1) == INVALID
+    assert lib.gqla_mqa_absorb_workspace_bytes(None, 3, 0) == 0
+    assert lib.gqla_mqa_absorb_workspace_bytes(ctypes.byref(d), 3, -1) == 0
 
 
 def test_expand_and_combine_argument_errors(lib):

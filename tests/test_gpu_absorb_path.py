@@ -159,21 +159,32 @@ def test_absorb_is_deterministic_and_writes_only_its_outputs():
 
 
 def test_absorb_partials_match_oracle_partials():
-    # the per-split outputs (already up-projected by W_UV) before the merge
-    from oracle.gqla_ref import decode_partials
-    log("absorb/partials")
-    case = config_case("dsv3", 1, batch=2, ctx=(700, 130), poison=True, table="random")
+    # the per-split latent outputs o_lat and their lse, as the decode kernel
+    # leaves them in the workspace before the merge and the up-projection
+    from oracle.gqla_ref import decode_partials_latent
+    log("absorb/latent partials")
+    case = config_case("dsv3", 2, batch=2, ctx=(700, 130), poison=True, table="random")
     gc = GpuCase(case)
     d = gc.d
     offs, total, st = gc.split(256)
-    po = torch.empty(total, 1, d.num_heads, d.d_v, dtype=torch.float32, device="cuda")
-    pl = torch.empty(total, 1, d.num_heads, dtype=torch.float32, device="cuda")
+    ws = G.absorb_workspace(d, 2, total_splits=total)
+    out = torch.empty(2, d.s_q, d.num_heads, d.d_v, dtype=torch.bfloat16, device="cuda")
     G.gqla_decode_mqa_absorb(d, gc.q_nope, gc.q_rope, gc.pages, gc.block_table, gc.seqlens,
-                             gc.w_uk, gc.w_uv, split_offsets=offs, split_tokens=st,
-                             total_splits=total, part_out=po, part_lse=pl,
-                             workspace=G.absorb_workspace(d, 2))
+                             gc.w_uk, gc.w_uv, out=out, split_offsets=offs, split_tokens=st,
+                             total_splits=total, workspace=ws)
     torch.cuda.synchronize()
-    ref_po, ref_pl, ref_off = decode_partials(*oracle_args(case), dims_of(case), 256)
+    o0, o1, o2, o3 = G.gqla_mqa_absorb_workspace_offsets(d, 2, total)
+    rows = d.s_q * d.num_heads
+    lat = ws[o2:o2 + total * rows * d.d_latent * 2].view(torch.bfloat16)
+    lat = lat.view(total, d.s_q, d.num_heads, d.d_latent)
+    lse = ws[o3:o3 + total * rows * 4].view(torch.float32).view(total, d.s_q, d.num_heads)
+    q_nope, q_rope, pages, bt, sl, w_uk, _ = oracle_args(case)
+    ref_lat, ref_lse, ref_off = decode_partials_latent(q_nope, q_rope, pages, bt, sl, w_uk,
+                                                       dims_of(case), 256)
     assert list(ref_off) == offs.cpu().tolist()
-    assert_close(po.cpu().double().numpy(), ref_po, "partial outputs")
-    assert_lse_close(pl.cpu().double().numpy(), ref_pl, "partial lse")
+    got_lat, got_lse = f64(lat), f64(lse)
+    empty = ~np.isfinite(ref_lse)            # rows that see no token of a split (MTP row 0)
+    assert np.array_equal(empty, ~np.isfinite(got_lse))
+    assert np.all(got_lat[empty] == 0)
+    assert_close(got_lat[~empty], ref_lat[~empty], "latent partials")
+    assert_lse_close(got_lse[~empty], ref_lse[~empty], "partial lse")

@@ -18,7 +18,7 @@ import torch
 from decode_attention_gqla_amd.inputs import make_case, random_partials
 from oracle import brute
 from oracle.gqla_ref import (Dims, bf16_round, combine, decode_absorb_form, decode_gqa_expanded,
-                             decode_literal, decode_partials, expand_pages, expanded_offset_k,
+                             decode_literal, decode_partials, decode_partials_latent, expand_pages, expanded_offset_k,
                              expanded_offset_rope, expanded_offset_v, expanded_page_elems,
                              _expanded_group_views, _expanded_rope_view, gather_latent)
 from tests.oracle_util import dims_of, oracle_args
@@ -227,6 +227,33 @@ def test_merge_of_partials_equals_unsplit(split_tokens):
     o, l = combine(po, pl, off)
     assert rel(o, ref_o) < 1e-13
     assert np.max(np.abs(l - ref_l)) < 1e-13
+
+
+@pytest.mark.parametrize("s_q", [1, 2])
+def test_latent_partials_up_project_to_the_literal_partials(s_q):
+    # the absorb path's split partials are taken in the latent space; by
+    # linearity o_lat W_UV[G] must be the literal form's split output, with the
+    # same lse, and merging in the latent space before the up-projection must
+    # give the unsplit result
+    case = tiny_case((47, 130, 17), s_q, seed=64)
+    d = dims_of(case)
+    args = oracle_args(case)
+    q_nope, q_rope, pages, bt, sl, w_uk, w_uv = args
+    pl_lat, pl_lse, off = decode_partials_latent(q_nope, q_rope, pages, bt, sl, w_uk, d, 16)
+    po, pl, off2 = decode_partials(*args, d, 16)
+    assert list(off) == list(off2)
+    w_uv = np.asarray(w_uv, np.float64)
+    G_of_h = np.arange(d.h_q) // d.heads_per_group
+    up = np.einsum("sihr,hrv->sihv", pl_lat, w_uv[G_of_h])
+    assert rel(up, po) < 1e-12
+    fin = np.isfinite(pl)
+    assert np.array_equal(fin, np.isfinite(pl_lse))
+    assert np.max(np.abs(pl_lse[fin] - pl[fin])) < 1e-12
+    assert np.all(pl_lat[~fin] == 0)
+    o_lat, l = combine(pl_lat, pl_lse, off)
+    ref_o, ref_l = decode_literal(*args, d)
+    assert rel(np.einsum("bihr,hrv->bihv", o_lat, w_uv[G_of_h]), ref_o) < 1e-12
+    assert np.max(np.abs(l - ref_l)) < 1e-12
 
 
 def test_partial_with_no_visible_token_is_empty():
