@@ -54,7 +54,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--absorb-split", type=int, default=1024,
+    ap.add_argument("--absorb-split", type=int, default=2048,
                     help="tokens per split-KV partition of the absorb path (0 = no split)")
     ap.add_argument("--gqa-split", type=int, default=0,
                     help="tokens per split-KV partition of the GQA path (0 = no split)")

@@ -54,7 +54,7 @@ namespace gqla {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+__device__ __forceinline__ f32x16 mfma16x32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
@@ -80,48 +80,68 @@ template <int HPG, int SQ, int R, int DR, int DN, int DV>
 struct AbsorbCfg {
   static constexpr int BS = 64;
   static constexpr int TILE = 32;                 // tokens per LDS tile
-  static constexpr int NBUF = 4;                  // tile buffers (the copy of tile it+3 goes out at step it)
+  static constexpr int NBUF = 4;                  // tile buffers
   static constexpr int ROW = R + DR;              // latent row (elements)
   static constexpr int CHR = ROW / 8;             // 16-byte chunks per token row
   static constexpr bool SWZ = (CHR % 8) == 0;     // XOR swizzle stays inside a row
   static constexpr int BUF_BYTES = TILE * ROW * 2;
   static constexpr int NI = TILE * CHR / 64;      // wave-wide DMA instructions per tile
-  static constexpr int NW = 4;                    // waves per workgroup (one per SIMD)
-  static constexpr int NIW = (NI + NW - 1) / NW;  // most DMA instructions of one wave per tile
-  static constexpr int ROWS_W = 32;               // query rows per wave
-  static constexpr int ROWS_WG = NW * ROWS_W;
-  static constexpr int KQ = ROW / 16;             // k steps of S^T = C Q^T
+  static constexpr int NQW = 4;                   // QK waves (one per SIMD)
+  static constexpr int NPW = 4;                   // PV waves (one per SIMD); they also issue the copies
+  static constexpr int NW = NQW + NPW;
+  static constexpr int NIW = (NI + NPW - 1) / NPW;  // most copy instructions of one PV wave per tile
+  static constexpr int ROWS_QW = 16;              // query rows per QK wave
+  static constexpr int ROWS_WG = NQW * ROWS_QW;   // query rows per workgroup
+  static constexpr int KQ = (ROW + 31) / 32;      // k steps of S^T = C Q^T (16x16x32)
   static constexpr int MT = R / 32;               // 32-dim tiles of O^T
-  static constexpr int MD = DV / 16;              // 16-dim tiles of the output
+  static constexpr int MTW = (MT + NPW - 1) / NPW;  // O tiles per PV wave (wave v: tiles v, v + NPW, ...)
+  static constexpr int NTR = ROWS_WG / 32;        // 32-row tiles of O^T
   static constexpr int OL_STRIDE = 2 * R + 16;    // LDS row stride of the staged o_lat (bytes)
-  static constexpr int OFF_VOTE = NBUF * BUF_BYTES;          // restart votes [2 slots][NW waves]
-  static constexpr int LDS_BYTES = OFF_VOTE + 32;
+  static constexpr int P_BYTES = 2 * ROWS_WG * 32;           // P^T of one tile: [k step][row][16 tokens] bf16
+  static constexpr int OFF_P = NBUF * BUF_BYTES;             // P^T, two tiles (double buffer)
+  static constexpr int OFF_VOTE = OFF_P + 2 * P_BYTES;       // restart votes [2 slots][NQW]
+  static constexpr int OFF_L = OFF_VOTE + 32;                // row sums [ROWS_WG] (fp32)
+  static constexpr int LDS_BYTES = OFF_L + ROWS_WG * 4;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-  static_assert(NW * ROWS_W * OL_STRIDE <= NBUF * BUF_BYTES, "o_lat staging fits in the tile buffers");
+  static_assert(ROWS_WG * OL_STRIDE <= NBUF * BUF_BYTES, "o_lat staging fits in the tile buffers");
   static_assert((TILE * CHR) % 64 == 0, "tile must be whole DMA instructions");
   static_assert(ROW % 16 == 0 && R % 32 == 0 && DN % 32 == 0 && DV % 16 == 0, "unsupported dims");
-  static_assert(NIW * 2 <= 63, "vmcnt budget");
+  static_assert(NIW <= 31, "vmcnt budget");
+  static_assert(ROWS_WG % 32 == 0, "row tiles");
 };
 
 // Swizzle of 16-byte chunk positions inside a token row (tokens 0..31 of a
-// tile; requires 8 | chunks per row).  gfx950 LDS has 64 four-byte banks; a
-// 16-byte read is served in four passes of 16 lanes (per half wave, the
-// 4-lane quads of even bit parity and those of odd parity), an 8-byte or
-// transposing read in two passes of 32 lanes.  With a 1152-byte token row,
-// token t starts at bank slot 8 (t & 1) (16-byte slots mod 16).  XOR-ing the
-// low three chunk bits with f(t) = 4 ((t >> 1) & 1) + ((t >> 3) & 3) gives:
-//   * QK reads (one chunk of 16 tokens per pass): (t & 1, f(t)) is distinct
-//     over the tokens of each pass, so the 16 slots are distinct;
-//   * PV transposing reads (4 consecutive tokens x 4 chunks per pass): tokens
-//     t and t + 2 differ in bit 2 of f, so their chunk quads land on disjoint
-//     slots, and t, t + 1 differ in the slot's bit 3.
-__device__ __forceinline__ int tile_swz(int t) { return 4 * ((t >> 1) & 1) + ((t >> 3) & 3); }
+// tile; requires 8 | chunks per row): the low three chunk bits are XOR-ed with
+// f(t) = 4 ((t >> 1) & 1) + 2 ((t >> 2) & 1).  gfx950 LDS has 64 four-byte
+// banks; a 16-byte read is served in four passes of 16 lanes (per half wave,
+// the 4-lane quads of even bit parity and those of odd parity), an 8-byte or
+// transposing read in two passes of 32 lanes.  With a 1152-byte token row
+// (token t starts at 16-byte slot 8 (t & 1) mod 16) this f makes every pass of
+// both readers hit 64 distinct banks: the QK reads (16 tokens x 4 consecutive
+// chunks per instruction) and the PV transposing reads (4 consecutive tokens x
+// 4 chunks per pass), checked exhaustively against that pass model over all
+// chunk offsets.
+__device__ __forceinline__ int tile_swz(int t) { return 4 * ((t >> 1) & 1) + 2 * ((t >> 2) & 1); }
 
+// Decode kernel, one workgroup of eight waves per (split of a sequence, block
+// of 64 query rows); two waves per SIMD with complementary work, so one
+// wave's memory and LDS latency is covered by the other's MFMAs:
+//   * QK waves 0..3 (16 rows each, 16x16x32 MFMA): their query rows stay in
+//     registers; S^T = C_tile Q^T per 32-token tile; the online softmax; the
+//     bf16 P^T of the tile into LDS (double-buffered);
+//   * PV waves 4..7: O^T += C^T P^T for the previous tile on the 32x32x16
+//     MFMA, each wave over its 32-dim tiles of the latent and all 64 rows
+//     (O in the accumulation registers; C^T by the transposing LDS read, P^T
+//     from LDS); they also issue the HBM -> LDS copies of the tiles.
+// One workgroup barrier per tile; phase it runs QK + softmax of tile it and
+// PV of tile it-1.  The latent tiles go HBM -> LDS by direct DMA
+// (global_load_lds_dwordx4, four buffers, two tiles in flight).
 template <int HPG, int SQ, int R, int DR, int DN, int DV>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void absorb_decode_kernel(DecodeParams p) {
   using C = AbsorbCfg<HPG, SQ, R, DR, DN, DV>;
-  constexpr int BS = C::BS, ROW = C::ROW, CHR = C::CHR, KQ = C::KQ, MT = C::MT, MD = C::MD, NW = C::NW;
+  constexpr int BS = C::BS, ROW = C::ROW, CHR = C::CHR, KQ = C::KQ, MT = C::MT, NQW = C::NQW;
+  constexpr int NPW = C::NPW;
   __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[C::LDS_BYTES];
   lds_u8_t* const lds = (lds_u8_t*)lds_raw;
 
@@ -131,8 +151,8 @@ void absorb_decode_kernel(DecodeParams p) {
   const int RB = (rows_total + C::ROWS_WG - 1) / C::ROWS_WG;
   // Workgroups are dispatched round-robin over the 8 XCDs.  XCD x takes the
   // contiguous unit range [x * UPX, (x + 1) * UPX), so the splits of one
-  // sequence (consecutive units) share an L2 for their query rows, and the
-  // row blocks of one unit take consecutive slots on one XCD.
+  // sequence share an L2 for their query rows, and the row blocks of one unit
+  // (which copy the same latent tiles) take consecutive slots on one XCD.
   const int UPX = (p.num_units + 7) / 8;
   const int wg = blockIdx.x;
   const int xcd = wg & 7, k = wg >> 3;
@@ -142,7 +162,10 @@ void absorb_decode_kernel(DecodeParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
+  const bool is_qk = w < NQW;
+  const int v = is_qk ? 0 : w - NQW;              // PV wave index
   const int hh = lane >> 5;                       // half wave
+  const int c = lane & 15, qq = lane >> 4;        // 16x16 MFMA lane coordinates
   int b, lo, hi;
   if (p.split_offsets) {
     b = split_owner(p.split_offsets, p.batch, u);
@@ -161,337 +184,327 @@ void absorb_decode_kernel(DecodeParams p) {
   const int n_tiles = hi > lo ? (hi - lo + C::TILE - 1) / C::TILE : 0;
   const int32_t* bt = p.block_table + (size_t)b * p.max_blocks;     // wave-uniform
 
-  // ---- HBM -> LDS tile copies: wave w issues instructions w, w+4, ... ----
-  // Block-table entries are read through the scalar cache (constant address
-  // space, wave-uniform index).  LDS position P (16-byte chunk index inside
-  // the tile) holds token P / CHR, physical chunk P % CHR, i.e. logical chunk
-  // (P % CHR) ^ f(token); the per-lane source offsets are the same for every
-  // tile and are computed once.
+  // ---- HBM -> LDS tile copies by the PV waves: wave v issues instructions
+  // v, v + NPW, ... of a tile.  LDS position P (16-byte chunk index inside the
+  // tile) holds token P / CHR, physical chunk P % CHR, i.e. logical chunk
+  // (P % CHR) ^ f(token); the per-lane source offsets are computed once.
   typedef const __attribute__((address_space(4))) int32_t cint32_t;
   const cint32_t* const cbt = (const cint32_t*)bt;
-  constexpr bool kFixedCopies = (C::NI % NW) == 0;   // every wave issues NIW copies per tile
-  const int niw = kFixedCopies ? C::NIW : (C::NI - w + NW - 1) / NW;
+  constexpr bool kFixedCopies = (C::NI % NPW) == 0;  // every PV wave issues NIW copies per tile
+  const int niw = kFixedCopies ? C::NIW : (C::NI - v + NPW - 1) / NPW;
   uint32_t dvo[C::NIW];
 #pragma unroll
   for (int kk = 0; kk < C::NIW; ++kk) {
-    const int i = min(w + NW * kk, C::NI - 1);
+    const int i = min(v + NPW * kk, C::NI - 1);
     const int P = i * 64 + lane;
     const int t = P / CHR, pos = P % CHR;
     const int ch = C::SWZ ? (pos ^ tile_swz(t)) : pos;
     dvo[kk] = (uint32_t)(t * ROW + ch * 8) * 2u;
   }
-  struct Copy {
-    const uint16_t* src;
-    lds_u8_t* dst;
-  };
-  auto copy_of = [&](int it) -> Copy {
+  auto tile_page = [&](int it) -> int { return cbt[(lo + C::TILE * it) / BS]; };
+  // Copy of tile it from page `page` (its block-table entry).  In the
+  // sequence's last tile the rows past its end copy the last token's row
+  // instead of the page's unused slots, which may hold anything: their logits
+  // are masked, so their P is 0, and 0 times a finite row adds nothing to O
+  // (0 times a NaN would).
+  auto issue_tile = [&](int it, int page) {       // PV waves only
     const int t0 = lo + C::TILE * it;
-    const int page = cbt[t0 / BS];
-    return Copy{p.cache + ((size_t)page * BS + (t0 % BS)) * ROW, lds + (it % C::NBUF) * C::BUF_BYTES};
-  };
-  auto copy_part = [&](const Copy& cp, int kk) {  // instruction kk of this wave (kk < niw)
-    dma16(cp.src, dvo[kk], cp.dst + (w + NW * kk) * 1024);
-  };
-
-  // The copies of tiles 0, 1 and 2 go out first; the query loads follow.
-  auto issue_head = [&]() {
-    for (int i = 0; i < C::NBUF - 1 && i < n_tiles; ++i) {
-      const Copy cp = copy_of(i);
-      for (int kk = 0; kk < niw; ++kk) copy_part(cp, kk);
+    const uint16_t* src = p.cache + ((size_t)page * BS + (t0 % BS)) * ROW;
+    lds_u8_t* dst = lds + (it % C::NBUF) * C::BUF_BYTES;
+    if (t0 + C::TILE <= L) {
+      for (int kk = 0; kk < niw; ++kk) dma16(src, dvo[kk], dst + (v + NPW * kk) * 1024);
+    } else {
+      const int last = L - t0 - 1;                // last valid row of the tile
+      for (int kk = 0; kk < niw; ++kk) {
+        const int t = (min(v + NPW * kk, C::NI - 1) * 64 + lane) / CHR;
+        dma16(src, dvo[kk] - (uint32_t)(max(t - last, 0) * ROW * 2), dst + (v + NPW * kk) * 1024);
+      }
     }
   };
-  issue_head();
+  auto pv_wait_next = [&](int it) {               // PV waves: tile it + 1 landed (tile it + 2 may be in flight)
+    if (it + 1 >= n_tiles) return;
+    if (it + 2 < n_tiles) {
+      if constexpr (kFixedCopies) vm_wait<C::NIW>(); else vm_wait_dyn(niw);
+    } else {
+      vm_wait<0>();
+    }
+  };
 
-  // ---- this wave's query rows: lane l holds row row0 + l%32 ----
-  const int row0 = rb * C::ROWS_WG + C::ROWS_W * w;
-  const bool active = row0 < rows_total;          // wave-uniform
-  const int rq = row0 + (lane & 31);
-  const bool rvalid = rq < rows_total;
+  // ---- QK waves: query rows rb * 64 + 16 w + c ----
+  const int rl = C::ROWS_QW * w + c;              // row inside the workgroup (QK waves)
+  const int rq = rb * C::ROWS_WG + rl;
+  const bool rvalid = is_qk && rq < rows_total;
+  const bool qk_active = is_qk && rb * C::ROWS_WG + C::ROWS_QW * w < rows_total;   // wave-uniform
   const int h_q = rvalid ? rq / SQ : 0, i_q = rvalid ? rq % SQ : 0;
   const int nvis = rvalid ? L - SQ + i_q + 1 : -1;  // tokens t < nvis are visible to this row
-  bf16x8 qb[KQ];                                  // B operands: Q[row][16 ks + 8 hh .. +7]
-  {
-    const uint16_t* qrow = p.qcat + (((size_t)b * SQ + i_q) * H + h_q) * ROW;
-#pragma unroll
-    for (int ks = 0; ks < KQ; ++ks) qb[ks] = rvalid ? ld_bf16x8(qrow + 16 * ks + 8 * hh) : zero_bf16x8();
-  }
+  const int ntv = min(C::NTR, (rows_total - rb * C::ROWS_WG + 31) / 32);   // row tiles with rows
 
-  // Per-lane LDS byte offsets of the MFMA operands inside a tile buffer.
-  // QK A operand of k step ks: token lane%32, logical chunk 2 ks + hh, which
-  // sits at 8 (ks >> 2) + ((2 (ks & 3) + hh) ^ f): one base per ks & 3, the
-  // rest an immediate of 128 (ks >> 2) bytes.
-  const int tq = lane & 31;
-  int qkb[4];
+  // QK A operand of token half st, k step ks: token 16 st + c, logical chunk
+  // 4 ks + qq, at 8 (ks >> 1) + ((4 (ks & 1) + qq) ^ f): one base per
+  // (st, ks & 1), the rest an immediate of 128 (ks >> 1) bytes.
+  int qkb[2][2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int ch = C::SWZ ? ((2 * j + hh) ^ tile_swz(tq)) : (2 * j + hh);
-    qkb[j] = tq * ROW * 2 + ch * 16;
-  }
-  auto qk_addr = [&](int ks) -> int {
-    return C::SWZ ? qkb[ks & 3] + 128 * (ks >> 2) : qkb[0] + 32 * ks;
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp) {
+      const int t = 16 * st + c;
+      const int ch = C::SWZ ? ((4 * kp + qq) ^ tile_swz(t)) : (4 * kp + qq);
+      qkb[st][kp] = t * ROW * 2 + ch * 16;
+    }
+  auto qk_operand = [&](const lds_u8_t* buf, int st, int ks) -> bf16x8 {
+    if (32 * ks + 8 * qq >= ROW) return zero_bf16x8();      // past the row (narrow shapes)
+    const int addr = C::SWZ ? qkb[st][ks & 1] + 128 * (ks >> 1) : qkb[st][0] + 64 * ks;
+    return __builtin_bit_cast(bf16x8, *(const lds_u32x4_t*)(buf + addr));
   };
-  // PV A operand (C^T, 32 latent dims x 16 tokens) of tile mt, k step kk:
-  // k index 8 hh + j stands for token 16 kk + 8 (j / 4) + 4 hh + j % 4, the
-  // order in which the S^T accumulators hold the tokens.  Two transposing
+  // PV A operand (C^T, 32 latent dims x 16 tokens) of dim tile mt = v + NPW m,
+  // k step kk: k index 8 hh + j is token 16 kk + 8 hh + j.  Two transposing
   // reads (rd = j / 4); in read rd the 16-lane group gq = lane / 16 reads
-  // tokens 16 kk + 8 rd + 4 (gq / 2) + s / 4 (s = lane % 16), dims
+  // tokens 16 kk + 8 (gq / 2) + 4 rd + s / 4 (s = lane % 16), dims
   // 32 mt + 16 (gq % 2) + 4 (s % 4) .. +3, so lane s receives dim
   // 32 mt + 16 (gq % 2) + s of four consecutive tokens.  Logical chunk
   // 4 mt + x (x = 2 (gq % 2) + (s % 4) / 2) sits at
-  // 4 (mt ^ (s >> 3)) + (x ^ (rd + 2 kk)) under the swizzle: one base per
-  // (rd, kk, mt & 1), the rest an immediate of 128 (mt >> 1) bytes.
+  // 8 (mt >> 1) + ((4 (mt & 1) + x) ^ f); mt & 1 = v & 1 for every tile of the
+  // wave, so one base per (rd, kk), plus 128 (mt >> 1) bytes.
   const int gq = lane >> 4, s16 = lane & 15;
-  int pvb[2][2][2];
+  int pvb[2][2];
 #pragma unroll
   for (int rd = 0; rd < 2; ++rd)
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int mp = 0; mp < 2; ++mp) {
-        const int t = 16 * kk + 8 * rd + 4 * (gq >> 1) + (s16 >> 2);
-        const int x = 2 * (gq & 1) + ((s16 & 3) >> 1);
-        const int ch = C::SWZ ? 4 * (mp ^ ((s16 >> 3) & 1)) + (x ^ (rd + 2 * kk)) : 4 * mp + x;
-        pvb[rd][kk][mp] = t * ROW * 2 + ch * 16 + 8 * (s16 & 1);
-      }
-  auto pv_operand = [&](const lds_u8_t* buf, int mt, int kk) -> bf16x8 {
-    const int imm = C::SWZ ? 128 * (mt >> 1) : 128 * (mt >> 1);
-    const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(buf + pvb[0][kk][mt & 1] + imm));
-    const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(buf + pvb[1][kk][mt & 1] + imm));
+    for (int kk = 0; kk < 2; ++kk) {
+      const int t = 16 * kk + 8 * (gq >> 1) + 4 * rd + (s16 >> 2);
+      const int x = 2 * (gq & 1) + ((s16 & 3) >> 1);
+      const int lowc = 4 * (v & 1) + x;
+      const int ch = C::SWZ ? (lowc ^ tile_swz(t)) : lowc;
+      pvb[rd][kk] = t * ROW * 2 + ch * 16 + 8 * (s16 & 1) + 128 * (v >> 1);
+    }
+  auto pv_operand = [&](const lds_u8_t* buf, int m, int kk) -> bf16x8 {
+    const int imm = 256 * m;                      // mt >> 1 = (v >> 1) + 2 m
+    const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(buf + pvb[0][kk] + imm));
+    const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(buf + pvb[1][kk] + imm));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
   };
+  // P^T of tile it in LDS: [k step][row][16 tokens] bf16, 32 bytes per row
+  // with its two 16-byte halves swapped on rows 8..15 of every 16 (so the PV
+  // reads of 16 rows hit distinct banks).
+  auto p_off = [&](int it, int kk, int row, int half) -> int {
+    return C::OFF_P + (it & 1) * C::P_BYTES + (kk * C::ROWS_WG + row) * 32 + 16 * (half ^ ((row >> 3) & 1));
+  };
 
-  // Softmax reference.  A row's reference is the maximum of its first tile
-  // and then stays fixed, so the O accumulators are only ever written by
-  // MFMAs (a rescale of the accumulation registers by the vector ALU would
-  // also make the compiler move them out of those registers).  Every
-  // p = 2^(x - ref) is kept below 2^kSlack: a tile whose logits exceed
-  // ref + kSlack on some row (an extreme logit spread, e.g. one dominant
-  // token) makes the workgroup restart the split: pass 1 sweeps QK for the
+  // Softmax reference: the maximum of a row's first tile, then fixed, so the
+  // O accumulators are only ever written by MFMAs.  Every p = 2^(x - ref) is
+  // kept below 2^kSlack: a tile whose logits exceed ref + kSlack on some row
+  // (an extreme logit spread, e.g. one dominant token) makes the workgroup
+  // restart the split before that tile's P is used: pass 1 sweeps QK for the
   // exact row maxima, pass 2 reruns the attention with them as the
   // references (then p <= 1).
   constexpr float kSlack = 64.f;
-  f32x16 o[MT];                                   // O^T: lane l = row l%32, latent 32 mt + 8 (i/4) + 4 hh + i%4
-  float m_ref = -INFINITY, l_run = 0.f;
-  bf16x8 pb[2];                                   // P^T operands of the previous tile (k steps 0, 1)
   typedef __attribute__((address_space(3))) int lds_i32_t;
-  // Restart votes, two slots of one int per wave: the vote of the softmax of
-  // tile it goes to slot (it + 1) & 1 (every wave stores its own entry every
-  // tile, so nothing needs resetting) and is read after the barrier of
-  // iteration it + 1; slot it & 1 is read right after the barrier of
-  // iteration it, which every wave has passed before any wave writes that
-  // slot again.
+  // restart votes of the QK waves, two slots: the softmax of tile it writes
+  // slot it & 1 before the barrier that ends phase it, every wave reads it in
+  // phase it + 1 (the PV waves first thing, the QK waves once their S reads
+  // are in flight), and it is next written in phase it + 2
   lds_i32_t* const votes = (lds_i32_t*)(lds + C::OFF_VOTE);
-  if (tid < 2 * NW) votes[tid] = 0;               // ordered before their reads by the first barrier
+  if (tid < 2 * NQW) votes[tid] = 0;
+  // Every wave reads the same votes between the same two barriers, so both
+  // roles take the same restart decision; their loops run the same barriers.
+  auto restart_requested = [&](int pass, int it) -> bool {
+    if (pass != 0 || it == 0) return false;       // votes of the softmax of tile it-1
+    const u32x4 vt = *(volatile lds_u32x4_t*)(lds + C::OFF_VOTE + 16 * ((it - 1) & 1));
+    return __builtin_amdgcn_readfirstlane((int)(vt[0] | vt[1] | vt[2] | vt[3])) != 0;
+  };
+  float* const l_lds = (float*)(lds_raw + C::OFF_L);
+  f32x16 o[C::MTW][C::NTR];                       // PV waves: O^T tile (v + NPW m, nt): lane l = row 32 nt + l%32,
+                                                  // latent 32 (v + NPW m) + 8 (i/4) + 4 hh + i%4
+  const int mtw = is_qk ? 0 : (MT - v + NPW - 1) / NPW;   // this PV wave's dim tiles
+  constexpr bool kAllDimTiles = (MT % NPW) == 0;  // every PV wave has MTW dim tiles
 
-  // Query loads and the first copies complete before the tile loop, so the
-  // compiler's own wait tracking has nothing pending inside it.
-  vm_wait<0>();
-
-  // Top of the step for tile it: tile it landed (the copies of tiles it+1
-  // and it+2, issued after it, may still be in flight; copies complete in
-  // order), then for every wave; the tail of the sequence's last tile is
-  // zeroed (token rows past its end hold anything, and 0 * NaN would still be
-  // NaN in the PV product).
-  auto tile_top = [&](int it) {
-    const int later = (it + 1 < n_tiles) + (it + 2 < n_tiles);
-    if constexpr (kFixedCopies) {
-      if (later == 2) vm_wait<2 * C::NIW>(); else if (later == 1) vm_wait<C::NIW>(); else vm_wait<0>();
-    } else {
-      vm_wait_dyn(later * niw);
-    }
-    block_sync_lds();
-    if (it < n_tiles && lo + C::TILE * (it + 1) > L) {
-      const int valid = L - (lo + C::TILE * it);
-      lds_u8_t* buf = lds + (it % C::NBUF) * C::BUF_BYTES;
-      for (int off = valid * ROW * 2 + tid * 16; off < C::BUF_BYTES; off += 64 * NW * 16)
-        *(lds_u32x4_t*)(buf + off) = u32x4{0u, 0u, 0u, 0u};
-      block_sync_lds();
-    }
-  };
-  // The copies of tile it+3 go out into the buffer of tile it-1 as soon as
-  // every wave is past its PV product (a barrier in the middle of step it),
-  // so three tiles are in flight for most of a step.
-  auto issue_ahead = [&](int it) {
-    if (it + C::NBUF - 1 < n_tiles) {
-      const Copy cp = copy_of(it + C::NBUF - 1);
-      for (int kk = 0; kk < niw; ++kk) copy_part(cp, kk);
-    }
-  };
-  // S^T of tile it over the full contraction
-  auto qk_tile = [&](int it) -> f32x16 {
-    f32x16 s = {};
-    const lds_u8_t* buf = lds + (it % C::NBUF) * C::BUF_BYTES;
-    auto qk_operand = [&](int ks) -> bf16x8 {
-      return __builtin_bit_cast(bf16x8, *(const lds_u32x4_t*)(buf + qk_addr(ks)));
-    };
-    constexpr int PD = 4;                         // operands read ahead
-    bf16x8 a[PD + 1];
+  if (is_qk) {
+    // =================== QK waves ===================
+    bf16x8 qb[KQ];                                // B operands: Q[row][32 ks + 8 qq .. +7]
+    {
+      const uint16_t* qrow = p.qcat + (((size_t)b * SQ + i_q) * H + h_q) * ROW;
 #pragma unroll
-    for (int j = 0; j < PD && j < KQ; ++j) a[j] = qk_operand(j);
-#pragma unroll
-    for (int j = 0; j < KQ; ++j) {
-      if (j + PD < KQ) a[(j + PD) % (PD + 1)] = qk_operand(j + PD);
-      s = mfma32(a[j % (PD + 1)], qb[j], s);
-    }
-    // schedule: the first PD operand reads, then per step the read of
-    // operand j + PD followed by the MFMA of step j
-    __builtin_amdgcn_sched_group_barrier(0x100, PD < KQ ? PD : KQ, 0);
-#pragma unroll
-    for (int j = 0; j < KQ; ++j) {
-      if (j + PD < KQ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    }
-    return s;
-  };
-  // visibility of lane l's 16 logits of tile it (token t0 + 8 (i / 4) + 4 hh + i % 4)
-  auto visible = [&](int it, int i) -> bool {
-    return lo + C::TILE * it + 8 * (i >> 2) + 4 * hh + (i & 3) < nvis;
-  };
-  auto pack_p = [&](const float (&x)[16], bf16x8 (&pn)[2]) {
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-      pn[kk] = __builtin_bit_cast(
-          bf16x8, u32x4{pack_bf16x2(x[8 * kk + 0], x[8 * kk + 1]), pack_bf16x2(x[8 * kk + 2], x[8 * kk + 3]),
-                        pack_bf16x2(x[8 * kk + 4], x[8 * kk + 5]), pack_bf16x2(x[8 * kk + 6], x[8 * kk + 7])});
-  };
-  float m_half = -INFINITY;                       // pass 1: running maximum of this lane's half row
-  for (int pass = 0; pass < 3; ++pass) {          // 0: single pass; 1, 2: after a restart
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) o[mt] = f32x16{};
-    l_run = 0.f;
-    if (pass > 0) issue_head();                   // the first tiles again after a restart
-    // ---- tile 0 of the split: sets each row's reference (pass 0) ----
-    float ps_prev = 0.f;                          // P sum of the previous tile
-    tile_top(0);
-    issue_ahead(0);                               // buffer 3 is still unused
-    if (active) {
-      const f32x16 s = qk_tile(0);
-      float x[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) x[i] = visible(0, i) ? s[i] * p.scale_log2 : -INFINITY;
-      float mx = x[0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
-      m_half = fmaxf(m_half, mx);
-      if (pass == 0) {
-        float a0 = mx, a1 = mx;
-        swap_pairs32(a0, a1);
-        m_ref = fmaxf(a0, a1);                    // -inf for a row that sees none of it
-      }
-      const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        x[i] = __builtin_amdgcn_exp2f(x[i] - m_use);
-        ps_prev += x[i];
-      }
-      pack_p(x, pb);
-    }
-    // ---- steps it = 1 .. n_tiles: S of tile it, the PV product of tile
-    // it-1, then the softmax of tile it ----
-    bool restart = false;
-    for (int it = 1; it <= n_tiles; ++it) {
-      tile_top(it);
-      // restart votes raised before this barrier (pass 0 only)
-      int flag = 0;
-      if (pass == 0) {
-        const u32x4 vt = *(volatile lds_u32x4_t*)(lds + C::OFF_VOTE + 16 * (it & 1));
-        flag = (int)(vt[0] | vt[1] | vt[2] | vt[3]);
-      }
-      f32x16 s = {};
-      if (it < n_tiles && active) s = qk_tile(it);
-      if (__builtin_amdgcn_readfirstlane(flag)) { // uniform over the workgroup
-        restart = true;
-        break;
-      }
-      if (active && pass != 1) {
-        l_run += ps_prev;
-        // O^T += C^T P^T for tile it-1
-        const lds_u8_t* buf = lds + ((it - 1) % C::NBUF) * C::BUF_BYTES;
-        constexpr int NS = 2 * MT;                // (kk, mt) steps
-        constexpr int PV = 4;
-        bf16x8 v[PV + 1];
-#pragma unroll
-        for (int j = 0; j < PV && j < NS; ++j) v[j] = pv_operand(buf, j % MT, j / MT);
-#pragma unroll
-        for (int j = 0; j < NS; ++j) {
-          if (j + PV < NS) v[(j + PV) % (PV + 1)] = pv_operand(buf, (j + PV) % MT, (j + PV) / MT);
-          o[j % MT] = mfma32(v[j % (PV + 1)], pb[j / MT], o[j % MT]);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * PV, 0);
-#pragma unroll
-        for (int j = 0; j < NS; ++j) {
-          if (j + PV < NS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        }
-      }
-      if (it == n_tiles) break;
-      block_sync_lds();                           // every wave is past PV of tile it-1
-      issue_ahead(it);
-      if (active) {
-        // Softmax of tile it, branch-free: masking by select, every row's
-        // reference fixed, no cross-lane step; each lane checks its own 16
-        // logits against ref + kSlack (the vote).
-        const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-        const float thr = m_ref + kSlack;
-        float x[16], mx = -INFINITY, ps = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const bool vis = visible(it, i);
-          const float xl = s[i] * p.scale_log2;
-          mx = fmaxf(mx, vis ? xl : -INFINITY);
-          x[i] = vis ? __builtin_amdgcn_exp2f(xl - m_use) : 0.f;
-          ps += x[i];
-        }
-        m_half = fmaxf(m_half, mx);
-        votes[NW * ((it + 1) & 1) + w] = __builtin_amdgcn_ballot_w64(mx > thr) != 0 ? 1 : 0;
-        ps_prev = ps;
-        pack_p(x, pb);
+      for (int ks = 0; ks < KQ; ++ks) {
+        const int dim = 32 * ks + 8 * qq;
+        qb[ks] = (rvalid && dim < ROW) ? ld_bf16x8(qrow + dim) : zero_bf16x8();
       }
     }
-    if (pass == 0 && !restart) break;             // the common case: done in one pass
-    if (pass == 1) {                              // the exact row maxima, for pass 2
-      float a0 = m_half, a1 = m_half;
-      swap_pairs32(a0, a1);
-      m_ref = fmaxf(a0, a1);
-    }
-    // drain this pass's copies before the tile buffers are refilled
+    float m_ref = -INFINITY, m_half = -INFINITY, l_run = 0.f;
     vm_wait<0>();
-    block_sync_lds();
-    if (pass == 0) m_half = -INFINITY;
+    block_sync_lds();                             // tiles 0 and 1 landed
+    for (int pass = 0; pass < 3; ++pass) {        // 0: single pass; 1, 2: after a restart
+      l_run = 0.f;
+      if (pass > 0) block_sync_lds();             // the first tiles landed again
+      bool restart = false;
+      for (int it = 0; it <= n_tiles; ++it) {
+        if (restart_requested(pass, it)) {
+          restart = true;
+          break;
+        }
+        f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        if (qk_active && it < n_tiles) {
+          // ---- S^T of tile it, two 16-token halves over the full contraction ----
+          const lds_u8_t* buf = lds + (it % C::NBUF) * C::BUF_BYTES;
+          constexpr int NS = 2 * KQ, PD = 8;    // operands read ahead
+          bf16x8 a[PD + 1];
+#pragma unroll
+          for (int j = 0; j < PD && j < NS; ++j) a[j] = qk_operand(buf, j & 1, j >> 1);
+#pragma unroll
+          for (int j = 0; j < NS; ++j) {
+            if (j + PD < NS) a[(j + PD) % (PD + 1)] = qk_operand(buf, (j + PD) & 1, (j + PD) >> 1);
+            s[j & 1] = mfma16(a[j % (PD + 1)], qb[j >> 1], s[j & 1]);
+          }
+          // schedule: the first PD operand reads, then per step the read of
+          // operand j + PD and the MFMA of step j (left to itself the
+          // compiler keeps only two reads in flight)
+          __builtin_amdgcn_sched_group_barrier(0x100, PD < NS ? PD : NS, 0);
+#pragma unroll
+          for (int j = 0; j < NS; ++j) {
+            if (j + PD < NS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          }
+        }
+        if (qk_active && it < n_tiles) {
+          // ---- softmax (base 2); lane (qq, c): tokens t0 + 16 st + 4 qq + e of row c ----
+          const int t0 = lo + C::TILE * it;
+          float x[8], mx = -INFINITY;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int st = e >> 2, ei = e & 3;
+            x[e] = (t0 + 16 * st + 4 * qq + ei < nvis) ? s[st][ei] * p.scale_log2 : -INFINITY;
+            mx = fmaxf(mx, x[e]);
+          }
+          m_half = fmaxf(m_half, mx);
+          if (it == 0 && pass == 0) m_ref = wave_max_q(mx);   // tile 0 sets each row's reference
+          if (pass != 1) {
+            // every row's reference is fixed from here on; each lane checks
+            // its own logits against ref + kSlack (the vote)
+            votes[4 * (it & 1) + w] = __builtin_amdgcn_ballot_w64(mx > m_ref + kSlack) != 0 ? 1 : 0;
+            const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+            float ps = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              x[e] = __builtin_amdgcn_exp2f(x[e] - m_use);
+              ps += x[e];
+            }
+            l_run += ps;
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+              const u32x2 pk = {pack_bf16x2(x[4 * st], x[4 * st + 1]), pack_bf16x2(x[4 * st + 2], x[4 * st + 3])};
+              *(__attribute__((address_space(3))) u32x2*)(lds + p_off(it, st, rl, qq >> 1) + 8 * (qq & 1)) = pk;
+            }
+          }
+        }
+        block_sync_lds();                         // end of phase it
+      }
+      if (pass == 0 && !restart) break;           // the common case: done in one pass
+      if (pass == 1) m_ref = wave_max_q(m_half);  // the exact row maxima, for pass 2
+      block_sync_lds();                           // end of the pass
+      if (pass == 0) m_half = -INFINITY;
+    }
+    // row sums and the lse
+    if (qk_active) {
+      const float lt = wave_sum_q(l_run);         // the four lane groups hold a row's token quarters
+      if (qq == 0) {
+        l_lds[rl] = lt;
+        if (rvalid) p.olse[((size_t)u * SQ + i_q) * H + h_q] = lt > 0.f ? (m_ref + log2f(lt)) * kLn2 : -INFINITY;
+      }
+    }
+  } else {
+    // =================== PV waves ===================
+    // Per phase it: the votes, the copy of tile it+2, then O^T += C^T P^T for
+    // tile it-1 (P^T and the transposed latent operands read from LDS).
+    bf16x8 ct[2][C::MTW];
+    auto load_ct = [&](int it) {
+      const lds_u8_t* buf = lds + (it % C::NBUF) * C::BUF_BYTES;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int m = 0; m < C::MTW; ++m)
+          ct[kk][m] = (kAllDimTiles || m < mtw) ? pv_operand(buf, m, kk) : zero_bf16x8();
+    };
+    for (int i = 0; i < 2 && i < n_tiles; ++i) issue_tile(i, tile_page(i));
+    vm_wait<0>();
+    block_sync_lds();                             // tiles 0 and 1 landed
+    for (int pass = 0; pass < 3; ++pass) {
+#pragma unroll
+      for (int m = 0; m < C::MTW; ++m)
+#pragma unroll
+        for (int nt = 0; nt < C::NTR; ++nt) o[m][nt] = f32x16{};
+      if (pass > 0) {                             // the first tiles again after a restart
+        for (int i = 0; i < 2 && i < n_tiles; ++i) issue_tile(i, tile_page(i));
+        vm_wait<0>();
+        block_sync_lds();
+      }
+      bool restart = false;
+      for (int it = 0; it <= n_tiles; ++it) {
+        if (restart_requested(pass, it)) {
+          restart = true;
+          break;
+        }
+        if (it + 2 < n_tiles) issue_tile(it + 2, tile_page(it + 2));   // into the buffer of tile it-2
+        const bool mult = it >= 1 && pass != 1 && mtw > 0;
+        // Straight-line code, no per-MFMA guard: a row tile past the last
+        // query row (nt >= ntv) multiplies whatever its P^T slots hold into
+        // accumulators that are never stored, and a dim tile past the
+        // latent (only when NPW does not divide MT) takes a zero operand.
+        if (mult) {
+          bf16x8 pt[2][C::NTR];
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int nt = 0; nt < C::NTR; ++nt)
+              pt[kk][nt] = __builtin_bit_cast(bf16x8, *(const lds_u32x4_t*)(lds + p_off(it - 1, kk, 32 * nt + (lane & 31), hh)));
+          load_ct(it - 1);
+          // this wave's dim tiles x every row tile
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int m = 0; m < C::MTW; ++m)
+#pragma unroll
+              for (int nt = 0; nt < C::NTR; ++nt) o[m][nt] = mfma16x32(ct[kk][m], pt[kk][nt], o[m][nt]);
+        }
+        pv_wait_next(it);
+        block_sync_lds();                         // end of phase it
+      }
+      if (pass == 0 && !restart) break;
+      vm_wait<0>();                               // drain before the tile buffers are refilled
+      block_sync_lds();                           // end of the pass
+    }
   }
 
   // ---- epilogue ----
-  // Every wave is past its last read of the tile buffers before any o_lat
-  // row is staged over them.
-  block_sync_lds();
-  if (!active) return;                            // no barrier follows
-  float lt = l_run;
-  {
-    float a0 = lt, a1 = lt;
-    swap_pairs32(a0, a1);
-    lt = a0 + a1;                                 // lanes l, l ^ 32 hold the two token halves of a row
-  }
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  if (hh == 0 && rvalid)
-    p.olse[((size_t)u * SQ + i_q) * H + h_q] = lt > 0.f ? (m_ref + log2f(lt)) * kLn2 : -INFINITY;
-  // normalised o_lat rows of this wave as bf16 in LDS: row r (of 32) at
-  // r * OL_STRIDE, latent-major; then one 1 KB row per store instruction
-  lds_u8_t* const ol = lds + w * C::ROWS_W * C::OL_STRIDE;
+  block_sync_lds();                               // row sums in LDS; every tile buffer read
+  // PV waves: normalised o_lat as bf16 in LDS over the tile buffers, row r at
+  // r * OL_STRIDE, latent-major
+  if (!is_qk) {
+    const int tq = lane & 31;
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+    for (int nt = 0; nt < C::NTR; ++nt) {
+      if (nt >= ntv) break;                       // uniform
+      const float lt = l_lds[32 * nt + tq];
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int lat = 32 * mt + 8 * a + 4 * hh;
-      const f32x16& om = o[mt];
-      u32x2 pk = {pack_bf16x2(om[4 * a] * inv, om[4 * a + 1] * inv), pack_bf16x2(om[4 * a + 2] * inv, om[4 * a + 3] * inv)};
-      *(__attribute__((address_space(3))) u32x2*)(ol + tq * C::OL_STRIDE + 2 * lat) = pk;
+      for (int m = 0; m < C::MTW; ++m) {
+        if (m >= mtw) break;                      // uniform
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int lat = 32 * (v + NPW * m) + 8 * a + 4 * hh;
+          const f32x16& om = o[m][nt];
+          u32x2 pk = {pack_bf16x2(om[4 * a] * inv, om[4 * a + 1] * inv), pack_bf16x2(om[4 * a + 2] * inv, om[4 * a + 3] * inv)};
+          *(__attribute__((address_space(3))) u32x2*)(lds + (32 * nt + tq) * C::OL_STRIDE + 2 * lat) = pk;
+        }
+      }
     }
-  for (int j = 0; j < C::ROWS_W; ++j) {
-    const int rho = row0 + j;                     // uniform
+  }
+  block_sync_lds();
+  // one 1 KB row per store instruction; wave w writes rows w, w + 8, ...
+  for (int j = w; j < C::ROWS_WG; j += C::NW) {
+    const int rho = rb * C::ROWS_WG + j;          // uniform
     if (rho >= rows_total) break;
     uint16_t* dst = p.olat + (((size_t)u * SQ + rho % SQ) * H + rho / SQ) * R;
     for (int e = lane; e < R / 8; e += 64)
-      *reinterpret_cast<u32x4*>(dst + 8 * e) = *(const lds_u32x4_t*)(ol + j * C::OL_STRIDE + 16 * e);
+      *reinterpret_cast<u32x4*>(dst + 8 * e) = *(const lds_u32x4_t*)(lds + j * C::OL_STRIDE + 16 * e);
   }
 }
 
@@ -787,7 +800,7 @@ hipError_t launch_absorb(const DecodeParams& p, hipStream_t stream) {
     const int RB = (rows_total + C::ROWS_WG - 1) / C::ROWS_WG;
     const unsigned grid = (unsigned)((p.num_units + 7) / 8) * 8u * (unsigned)RB;
     hipLaunchKernelGGL((absorb_decode_kernel<HPG, SQ, R, DR, DN, DV>), dim3(grid), dim3(64 * C::NW), 0,
-                       stream, p);
+                       stream, p);  // NW = 8 waves
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
