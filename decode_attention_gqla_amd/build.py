@@ -30,6 +30,9 @@ def flags() -> list[str]:
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         # packed fp32 VALU forms are kept out of the generated code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA accumulators in VGPRs: without it the GQA kernel copies its O
+        # tiles between VGPRs and AGPRs around every MFMA
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-I", os.path.join(ROOT, "include"), "-I", CSRC,
         "-Wno-unused-result",
     ]

@@ -5,13 +5,13 @@
 // decode runs conventional grouped-query attention, h_q/g heads x s_q query
 // rows per group, with the decoupled rope key shared by all groups.
 //
-// Work decomposition: one wave (one 64-lane workgroup) per (split unit, group).
-// The wave's query rows (h_q/g heads x s_q tokens, padded to 16-row tiles)
-// stay in registers.  Each 32-token tile of the group's K block, dim-major V
-// block and the shared rope key is copied HBM -> LDS by direct DMA
-// (global_load_lds_dwordx4, three tiles in flight per wave, no VGPR staging),
-// then read as bf16 MFMA operands (the copies are waited for explicitly with
-// vmcnt, see dma16):
+// Work decomposition: one workgroup per (split unit, group), one wave per
+// 16-row tile of the group's query rows (h_q/g heads x s_q tokens, padded),
+// which stay in registers.  Each 32-token tile of the group's K block,
+// dim-major V block and the shared rope key is copied HBM -> LDS by direct
+// DMA (global_load_lds_dwordx4, three tiles ahead, no VGPR staging; the waves
+// share the copy instructions and the tile), then read as bf16 MFMA operands
+// (the copies are waited for explicitly with vmcnt, see dma16):
 //   S^T[token][row] = K[token][:] . Q[row][:]        (A = cache rows, B = Q^T)
 //   O^T[dim][row]  += V^T[dim][token] . P^T[token][row]
 // The token order inside a tile is relabelled so that the S^T accumulator lane
@@ -19,6 +19,8 @@
 // holds tokens 8q..8q+7), and V^T is stored dim-major, so no operand needs a
 // transpose.  The LDS copies are XOR-swizzled in 16-byte chunks so every
 // operand read is bank-conflict free.
+#include <type_traits>
+
 #include "common.hip.h"
 #include "params.hip.h"
 
@@ -29,7 +31,8 @@ template <int HPG, int SQ, int DN, int DV, int DR>
 struct GqaCfg {
   static constexpr int BS = 64;
   static constexpr int TILE = 32;
-  static constexpr int NBUF = 3;
+  static constexpr int NBUF = 4;                  // tile buffers
+  static constexpr int LA = NBUF - 1;             // tiles in flight ahead of the one in use
   static constexpr int ROWS = HPG * SQ;
   static constexpr int NT = (ROWS + 15) / 16;     // 16-row tiles
   static constexpr int KSN = DN / 32;             // 32-wide k steps over d_nope
@@ -45,9 +48,14 @@ struct GqaCfg {
   static constexpr int NI_K = K_BYTES / 1024, NI_V = V_BYTES / 1024;
   static constexpr int NI_R = (R_BYTES + 1023) / 1024;
   static constexpr int NI = NI_K + NI_V + NI_R;   // DMA instructions per tile
+  static constexpr int NW = NT;                   // waves per workgroup, one per 16-row tile
+  static constexpr int NIW = NI / NW;             // DMA instructions per wave per tile
   static_assert(DN % 32 == 0 && DV % 16 == 0 && DR % 8 == 0, "unsupported head dims");
   static_assert(K_BYTES % 1024 == 0 && V_BYTES % 1024 == 0, "whole DMA instructions");
-  static_assert(2 * NI < 64, "vmcnt budget");
+  static_assert(NI % NW == 0, "the waves share the copies evenly");
+  static_assert(NW <= 2, "launch bound of 128 threads");
+  static_assert(LA * NIW < 64, "vmcnt budget");
+  static_assert(LA <= 3, "the in-flight wait covers up to two later tiles");
   static_assert((KCH & (KCH - 1)) == 0 && (RCH & (RCH - 1)) == 0, "power-of-two rows");
 };
 
@@ -62,9 +70,9 @@ __device__ __forceinline__ int rswz(int t) { return ((t >> 1) & 1) | ((t >> 3) <
 __device__ __forceinline__ int vswz(int d) { return 2 * ((d >> 2) & 1); }
 
 template <int HPG, int SQ, int DN, int DV, int DR>
-__global__ __launch_bounds__(64) void gqa_decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(128) void gqa_decode_kernel(DecodeParams p) {
   using C = GqaCfg<HPG, SQ, DN, DV, DR>;
-  constexpr int BS = C::BS, NT = C::NT, KSN = C::KSN, KSR = C::KSR, MT = C::MT;
+  constexpr int BS = C::BS, NW = C::NW, KSN = C::KSN, KSR = C::KSR, MT = C::MT;
   constexpr int KCH = C::KCH, RCH = C::RCH, VCH = C::VCH;
   __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[C::NBUF * C::TILE_BYTES];
   lds_u8_t* const lds = (lds_u8_t*)lds_raw;
@@ -81,7 +89,8 @@ __global__ __launch_bounds__(64) void gqa_decode_kernel(DecodeParams p) {
   if (u >= p.num_units) return;
 
   int b, lo, hi;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);   // this wave's 16-row tile
   if (p.split_offsets) {
     b = split_owner(p.split_offsets, p.batch, u);
     const int j = u - p.split_offsets[b];
@@ -98,7 +107,7 @@ __global__ __launch_bounds__(64) void gqa_decode_kernel(DecodeParams p) {
   const int n_tiles = hi > lo ? (hi - lo + C::TILE - 1) / C::TILE : 0;
   const int32_t* bt = p.block_table + (size_t)b * p.max_blocks;     // wave-uniform
 
-  // ---- DMA of tile `it` into `dst` (the buffer of tile it % 3) ----
+  // ---- DMA of tile `it` into `dst` (the buffer of tile it % NBUF) ----
   auto issue_tile = [&](int it) {
     lds_u8_t* dst = lds + (it % C::NBUF) * C::TILE_BYTES;
     const int t0 = lo + C::TILE * it;
@@ -107,20 +116,25 @@ __global__ __launch_bounds__(64) void gqa_decode_kernel(DecodeParams p) {
     const uint16_t* kblk = page + (size_t)G * BS * (DN + DV) + slot0 * DN;
     const uint16_t* vblk = page + (size_t)G * BS * (DN + DV) + BS * DN + slot0;
     const uint16_t* rope = page + (size_t)g * BS * (DN + DV) + slot0 * DR;
+    // copy instruction j of the tile (K, then V^T, then rope) is issued by
+    // wave j % NW
 #pragma unroll
     for (int i = 0; i < C::NI_K; ++i) {        // K rows: token-major, chunk swizzled
+      if (i % NW != w) continue;
       const int P = i * 64 + lane, t = P / KCH, pos = P % KCH;
       const int ch = pos ^ (kswz(t) & (KCH - 1));
       dma16(kblk, (uint32_t)(t * DN + ch * 8) * 2u, dst + i * 1024);
     }
 #pragma unroll
     for (int i = 0; i < C::NI_V; ++i) {        // V^T rows: 32 tokens of one dim
+      if ((C::NI_K + i) % NW != w) continue;
       const int P = i * 64 + lane, d = P / VCH, pos = P % VCH;
       const int ch = pos ^ vswz(d);
       dma16(vblk, (uint32_t)(d * BS + ch * 8) * 2u, dst + C::K_BYTES + i * 1024);
     }
 #pragma unroll
     for (int i = 0; i < C::NI_R; ++i) {        // rope rows: token-major, chunk swizzled
+      if ((C::NI_K + C::NI_V + i) % NW != w) continue;
       int P = i * 64 + lane;
       if (P >= C::TILE * RCH) P = C::TILE * RCH - 1;   // partial last instruction: duplicate
       const int t = P / RCH, pos = P % RCH;
@@ -129,70 +143,50 @@ __global__ __launch_bounds__(64) void gqa_decode_kernel(DecodeParams p) {
     }
   };
 
-  // Query rows of this group as B operands (Q^T): lane (q, c) holds 8 dims of row c.
-  bf16x8 qb[NT][KSN + KSR];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int rho = 16 * nt + c;
-    const bool valid = rho < C::ROWS;
-    const int hl = valid ? rho / SQ : 0, iq = valid ? rho % SQ : 0;
-    const int h = G * HPG + hl;
-    const size_t qrow = ((size_t)b * SQ + iq) * H + h;
+  // Query rows of this wave's tile as B operands (Q^T): lane (q, c) holds 8
+  // dims of row 16 w + c.
+  const int rho = 16 * w + c;
+  const bool rvalid = rho < C::ROWS;
+  bf16x8 qb[KSN + KSR];
+  {
+    const int hl = rvalid ? rho / SQ : 0, iq = rvalid ? rho % SQ : 0;
+    const size_t qrow = ((size_t)b * SQ + iq) * H + G * HPG + hl;
 #pragma unroll
     for (int ks = 0; ks < KSN; ++ks)
-      qb[nt][ks] = valid ? ld_bf16x8(p.q_nope + qrow * DN + 32 * ks + 8 * q) : zero_bf16x8();
+      qb[ks] = rvalid ? ld_bf16x8(p.q_nope + qrow * DN + 32 * ks + 8 * q) : zero_bf16x8();
 #pragma unroll
     for (int ks = 0; ks < KSR; ++ks) {
       const int dim = 32 * ks + 8 * q;
-      qb[nt][KSN + ks] = (valid && dim < DR) ? ld_bf16x8(p.q_rope + qrow * DR + dim) : zero_bf16x8();
+      qb[KSN + ks] = (rvalid && dim < DR) ? ld_bf16x8(p.q_rope + qrow * DR + dim) : zero_bf16x8();
     }
   }
 
   // The query loads complete before the first tile copy is issued, so the
   // compiler's own wait tracking has nothing pending inside the tile loop.
   vm_wait<0>();
-  if (n_tiles > 0) issue_tile(0);
-  if (n_tiles > 1) issue_tile(1);
+  for (int i = 0; i < C::LA && i < n_tiles; ++i) issue_tile(i);
 
-  f32x4 o[MT][NT];
-  float m_run[NT], l_run[NT];
-  int nvis[NT];
+  f32x4 o[MT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) o[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m_run[nt] = -INFINITY;
-    l_run[nt] = 0.f;
-    const int rho = 16 * nt + c;
-    nvis[nt] = L - SQ + (rho < C::ROWS ? rho % SQ : SQ - 1) + 1;
-  }
+  for (int mt = 0; mt < MT; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  const int nvis = L - SQ + (rvalid ? rho % SQ : SQ - 1) + 1;   // tokens t < nvis are visible
 
-  for (int it = 0; it < n_tiles; ++it) {
-    // prefetch tile it+2 into the buffer of tile it-1 (already consumed), then
-    // wait until tile it has landed
-    if (it + 2 < n_tiles) {
-      issue_tile(it + 2);
-      vm_wait<2 * C::NI>();
-    } else if (it + 1 < n_tiles) {
-      vm_wait<C::NI>();
-    } else {
-      vm_wait<0>();
-    }
-    const lds_u8_t* buf = lds + (it % C::NBUF) * C::TILE_BYTES;
-    const int t0 = lo + C::TILE * it;
-
-    f32x4 s[2][NT];
+  // One tile: S^T, the online softmax, O^T += V^T P^T.  EDGE: the tile
+  // reaches the causal bound or the sequence end, so logits are masked and
+  // the V rows of tokens past the end (which may hold anything) are zeroed.
+  auto tile_step = [&](const lds_u8_t* buf, int t0, auto edge) {
+    constexpr bool EDGE = decltype(edge)::value;
+    f32x4 s[2];
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const int t = 8 * (c >> 2) + 4 * st + (c & 3);     // token held by MFMA row c
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) s[st][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      s[st] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KSN; ++ks) {
         const int pos = (4 * ks + q) ^ (kswz(t) & (KCH - 1));
         const bf16x8 a = __builtin_bit_cast(bf16x8, *(const lds_u32x4_t*)(buf + (t * KCH + pos) * 16));
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) s[st][nt] = mfma16(a, qb[nt][ks], s[st][nt]);
+        s[st] = mfma16(a, qb[ks], s[st]);
       }
 #pragma unroll
       for (int ks = 0; ks < KSR; ++ks) {
@@ -202,102 +196,97 @@ __global__ __launch_bounds__(64) void gqa_decode_kernel(DecodeParams p) {
           const int pos = ch ^ (rswz(t) & (RCH - 1));
           a = __builtin_bit_cast(bf16x8, *(const lds_u32x4_t*)(buf + C::K_BYTES + C::V_BYTES + (t * RCH + pos) * 16));
         }
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) s[st][nt] = mfma16(a, qb[nt][KSN + ks], s[st][nt]);
+        s[st] = mfma16(a, qb[KSN + ks], s[st]);
       }
     }
-    // Online softmax (base 2).  Masking is needed only on tiles that reach
-    // the first causal bound (L - s_q + 1); the reference max moves lazily:
-    // the accumulators are rescaled only when some row's max exceeds its
-    // reference by more than 8 (so every p <= 2^8), which is rare after the
-    // first tile.
-    const bool masked = t0 + C::TILE > L - SQ + 1;
-    float x[NT][8], mx[NT];
+    // Online softmax (base 2) with a lazily moved reference max: the
+    // accumulators are rescaled only when the row's max exceeds its reference
+    // by more than 8 (so every p <= 2^8), which is rare after the first tile.
+    float x[8], mx = -INFINITY;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      mx[nt] = -INFINITY;
+    for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = s[st][nt][i] * p.scale_log2;
-          if (masked) v = (t0 + 8 * q + 4 * st + i < nvis[nt]) ? v : -INFINITY;
-          x[nt][4 * st + i] = v;
-          mx[nt] = fmaxf(mx[nt], v);
-        }
-      mx[nt] = wave_max_xor16_32(mx[nt]);
-    }
-    bool resc = false;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) resc |= mx[nt] > m_run[nt] + 8.f;
-    if (__any(resc)) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const float m_new = fmaxf(m_run[nt], mx[nt]);
-        const float alpha = (m_run[nt] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[nt] - m_new);
-        l_run[nt] *= alpha;
-        m_run[nt] = m_new;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) o[mt][nt] *= alpha;
+      for (int i = 0; i < 4; ++i) {
+        float v = s[st][i] * p.scale_log2;
+        if constexpr (EDGE) v = (t0 + 8 * q + 4 * st + i < nvis) ? v : -INFINITY;
+        x[4 * st + i] = v;
+        mx = fmaxf(mx, v);
       }
-    }
-    bf16x8 pb[NT];
+    mx = wave_max_q(mx);
+    if (__any(mx > m_run + 8.f)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+      m_run = m_new;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const float m_use = (m_run[nt] == -INFINITY) ? 0.f : m_run[nt];
+      for (int mt = 0; mt < MT; ++mt) o[mt] *= alpha;
+    }
+    bf16x8 pb;
+    {
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
       float ps = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        x[nt][j] = __builtin_amdgcn_exp2f(x[nt][j] - m_use);
-        ps += x[nt][j];
+        x[j] = __builtin_amdgcn_exp2f(x[j] - m_use);
+        ps += x[j];
       }
-      l_run[nt] += ps;
-      u32x4 pk = {pack_bf16x2(x[nt][0], x[nt][1]), pack_bf16x2(x[nt][2], x[nt][3]),
-                  pack_bf16x2(x[nt][4], x[nt][5]), pack_bf16x2(x[nt][6], x[nt][7])};
-      pb[nt] = __builtin_bit_cast(bf16x8, pk);
+      l_run += ps;
+      u32x4 pk = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+      pb = __builtin_bit_cast(bf16x8, pk);
     }
-    // tokens past the end of the sequence may hold anything: keep their V at 0
-    const bool tail = t0 + C::TILE > L;
-    const int keep = min(max(L - (t0 + 8 * q), 0), 8);
+    const int keep = EDGE ? min(max(L - (t0 + 8 * q), 0), 8) : 8;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int d = 16 * mt + c;
       const int pos = q ^ vswz(d);
       bf16x8 v = __builtin_bit_cast(bf16x8, *(const lds_u32x4_t*)(buf + C::K_BYTES + (d * VCH + pos) * 16));
-      if (tail) v = keep_first(v, keep);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) o[mt][nt] = mfma16(v, pb[nt], o[mt][nt]);
+      if constexpr (EDGE) v = keep_first(v, keep);
+      o[mt] = mfma16(v, pb, o[mt]);
     }
+  };
+
+  for (int it = 0; it < n_tiles; ++it) {
+    // this wave's copies of tile it landed (those of the next LA-1 tiles may
+    // be in flight); after the barrier every wave's copies of tile it landed
+    // and every wave is done with tile it-1, whose buffer takes tile it+LA
+    const int ahead = min(C::LA - 1, n_tiles - 1 - it);     // later tiles in flight
+    if (ahead == 2) vm_wait<2 * C::NIW>();
+    else if (ahead == 1) vm_wait<C::NIW>();
+    else vm_wait<0>();
+    if constexpr (NW > 1) __syncthreads();
+    if (it + C::LA < n_tiles) issue_tile(it + C::LA);
+    const lds_u8_t* buf = lds + (it % C::NBUF) * C::TILE_BYTES;
+    const int t0 = lo + C::TILE * it;
+    // only tiles that reach the first causal bound (L - s_q + 1), the last
+    // one or two of the sequence, mask logits and V rows
+    if (t0 + C::TILE > L - SQ + 1) tile_step(buf, t0, std::true_type{});
+    else tile_step(buf, t0, std::false_type{});
   }
 
-  // Epilogue: lane (q, c) holds dims 16*mt + 4q .. +3 of row 16*nt + c.
+  // Epilogue: lane (q, c) holds dims 16*mt + 4q .. +3 of row 16 w + c.
+  const float lt = wave_sum_q(l_run);
+  if (!rvalid) return;
+  const int hl = rho / SQ, iq = rho % SQ;
+  const int h = G * HPG + hl;
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const float lse_v = lt > 0.f ? (m_run + log2f(lt)) * kLn2 : -INFINITY;
+  if (p.split_offsets) {
+    const size_t row = ((size_t)u * SQ + iq) * H + h;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const float lt = wave_sum_xor16_32(l_run[nt]);
-    const int rho = 16 * nt + c;
-    if (rho >= C::ROWS) continue;
-    const int hl = rho / SQ, iq = rho % SQ;
-    const int h = G * HPG + hl;
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const float lse_v = lt > 0.f ? (m_run[nt] + log2f(lt)) * kLn2 : -INFINITY;
-    if (p.split_offsets) {
-      const size_t row = ((size_t)u * SQ + iq) * H + h;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const f32x4 v = o[mt][nt] * inv;
-        *reinterpret_cast<f32x4*>(p.part_out + row * DV + 16 * mt + 4 * q) = v;
-      }
-      if (q == 0) p.part_lse[row] = lse_v;
-    } else {
-      const size_t row = ((size_t)b * SQ + iq) * H + h;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const f32x4 v = o[mt][nt] * inv;
-        u32x2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        *reinterpret_cast<u32x2*>(p.out + row * DV + 16 * mt + 4 * q) = pk;
-      }
-      if (q == 0 && p.lse) p.lse[row] = lse_v;
+    for (int mt = 0; mt < MT; ++mt) {
+      const f32x4 v = o[mt] * inv;
+      *reinterpret_cast<f32x4*>(p.part_out + row * DV + 16 * mt + 4 * q) = v;
     }
+    if (q == 0) p.part_lse[row] = lse_v;
+  } else {
+    const size_t row = ((size_t)b * SQ + iq) * H + h;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const f32x4 v = o[mt] * inv;
+      u32x2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      *reinterpret_cast<u32x2*>(p.out + row * DV + 16 * mt + 4 * q) = pk;
+    }
+    if (q == 0 && p.lse) p.lse[row] = lse_v;
   }
 }
 
@@ -307,7 +296,8 @@ hipError_t launch_gqa(const DecodeParams& p, hipStream_t stream) {
   const int g = p.num_groups;
   const int rounds = (p.num_units + 7) / 8;
   const unsigned grid = (unsigned)rounds * 8u * (unsigned)g;
-  hipLaunchKernelGGL((gqa_decode_kernel<HPG, SQ, DN, DV, DR>), dim3(grid), dim3(64), 0, stream, p);
+  hipLaunchKernelGGL((gqa_decode_kernel<HPG, SQ, DN, DV, DR>), dim3(grid), dim3(64 * GqaCfg<HPG, SQ, DN, DV, DR>::NW), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
