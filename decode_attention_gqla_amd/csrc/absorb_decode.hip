@@ -15,9 +15,8 @@
 //      launch, W_UV^T [g][d_v][r] (the up-projection's A operand is then one
 //      16-byte load);
 //   2. absorb_decode_kernel: attention over the latent cache, one workgroup
-//      of four waves (one per SIMD, so each wave may hold 512 registers) per
-//      (split of a sequence, block of 128 query rows); it writes the split's
-//      normalised o_lat (bf16) and lse into the workspace;
+//      of eight waves per (split of a sequence, block of 64 query rows); it
+//      writes the split's normalised o_lat (bf16) and lse into the workspace;
 //   3. absorb_merge_kernel: per (group, block of sequences), the log-sum-exp
 //      merge of the splits' o_lat and the up-projection by W_UV[G].
 // The up-projection runs once per sequence after the merge (exact by
@@ -27,24 +26,18 @@
 //
 // Decode kernel.  Each 32-token latent tile (36 KB for r + d_R = 576) is
 // copied HBM -> LDS by direct DMA (global_load_lds_dwordx4; four tile buffers:
-// tile it is multiplied by Q, tile it-1 by P, tiles it+1 and it+2 in flight)
-// into an XOR-swizzled token-major layout.  Wave w owns 32 query rows end to
-// end, on the 32x32x16 bf16 MFMA:
-//   * its query rows (32 rows x the full r + d_R contraction) stay in
-//     registers as B operands;
-//   * S^T[32 tokens][32 rows] = C_tile Q^T: one 16-byte LDS read per MFMA;
-//   * online softmax inside the wave: lane l holds row l%32 and 16 of the 32
-//     tokens, so a row reduction is 16 in-lane values and one cross-half swap;
-//     relabelling the tokens inside each 16-token k step makes the S^T
-//     accumulators exactly the P^T B operands of the PV product;
-//   * O^T[latent][row] += C^T P^T over all r latent dims: the O accumulators
-//     (32 rows x 512 fp32) live in the accumulation registers; the C^T
-//     operands come from the transposing LDS read ds_read_b64_tr_b16.
-// One workgroup barrier per tile (copies landed, and the buffer refilled next
-// has been read by every wave).  PV of tile it-1 runs after QK of tile it, so
-// the softmax of tile it overlaps the PV MFMAs.
-// Epilogue: o_lat is normalised, staged as bf16 in LDS and written out one
-// full 1 KB row per store instruction.
+// tile it in QK, tile it-1 in PV, tiles it+1 and it+2 in flight) into an
+// XOR-swizzled token-major layout.  Two wave roles share every SIMD:
+//   * QK waves (16 query rows each, 16x16x32 MFMA): their query rows stay in
+//     registers as B operands; S^T = C_tile Q^T; the softmax against a fixed
+//     per-row reference; P^T as bf16 into LDS;
+//   * PV waves (32x32x16 MFMA): O^T[latent][row] += C^T P^T for their 4 of
+//     the 16 latent dim tiles and all 64 rows, O in accumulation registers,
+//     C^T from the transposing LDS read ds_read_b64_tr_b16; they also issue
+//     the tile copies.
+// One workgroup barrier per tile; phase it runs QK of tile it beside PV of
+// tile it-1.  Epilogue: o_lat is normalised, staged as bf16 in LDS and
+// written out one full 1 KB row per store instruction.
 #include <type_traits>
 
 #include "common.hip.h"
