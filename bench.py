@@ -234,6 +234,21 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic
     roof["kernel"] = dom
+    # the path selector on this batch: at the roofline, and with the fractions of it that
+    # each path just reached here
+    selector = None
+    if not args.only:
+        sel_d = G.Dims.make(128, 8, 512, 64, 128, 128, 1)
+        names = {G.PATH_ABSORB: "mqa_absorb", G.PATH_GQA: "gqa"}
+        at_roof, _, _ = G.gqla_select_path(sel_d, lens, 1, 2, G.Hw(rf.MI355X_HBM_GBPS, rf.MI355X_BF16_TFLOPS,
+                                                                    1.0, 1.0, 0))
+        fa = min(1.0, per_path["mqa_absorb"]["roofline_frac"])
+        fg = min(1.0, per_path["gqa"]["roofline_frac"])
+        measured, ea, eg = G.gqla_select_path(sel_d, lens, 1, 2, G.Hw(rf.MI355X_HBM_GBPS, rf.MI355X_BF16_TFLOPS,
+                                                                       fa, fg, 0))
+        selector = {"at_roofline": names[at_roof], "with_measured_fractions": names[measured],
+                    "frac_absorb": fa, "frac_gqa": fg,
+                    "tok_s_absorb": ea.tokens_per_s, "tok_s_gqa": eg.tokens_per_s}
     cpu = None
     if not args.no_cpu and not args.only:
         log("cpu oracle baseline")
@@ -253,6 +268,7 @@ def main():
         "cpu_baseline": cpu,
         "paths": per_path,
         "expand_us": t_expand_us,
+        "path_selector": selector,
         "kernel_source_hash": src_hash,
     }
     print(json.dumps(line))

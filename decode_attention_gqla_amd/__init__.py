@@ -53,6 +53,29 @@ class Dims(ctypes.Structure):
         return cls.make(case.h_q, case.g, case.r, case.d_R, case.d_nope, case.d_v, case.s_q, case.bs)
 
 
+class Hw(ctypes.Structure):
+    """gqla_hw: sustained HBM GB/s and bf16 matrix TFLOP/s, the fraction of the roofline each
+    path reaches, and the byte-counting convention (cache_only = the pages' step-time model)."""
+    _fields_ = [("hbm_gbps", ctypes.c_double), ("mfma_tflops", ctypes.c_double),
+                ("frac_absorb", ctypes.c_double), ("frac_gqa", ctypes.c_double),
+                ("cache_only", ctypes.c_int32)]
+
+
+class PathEstimate(ctypes.Structure):
+    """gqla_path_estimate: roofline estimate of one decode call of one path."""
+    _fields_ = [("bytes", ctypes.c_double), ("flops", ctypes.c_double),
+                ("t_hbm_us", ctypes.c_double), ("t_mfma_us", ctypes.c_double),
+                ("t_roofline_us", ctypes.c_double), ("t_expected_us", ctypes.c_double),
+                ("tokens_per_s", ctypes.c_double), ("bound", ctypes.c_int32)]
+
+    def as_dict(self) -> dict:
+        d = {k: getattr(self, k) for k, _ in self._fields_}
+        d["bound"] = "mfma" if self.bound else "hbm"
+        return d
+
+
+PATH_ABSORB, PATH_GQA = 0, 1
+
 _vp, _i32p, _f32p = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
 _SIGS = {
     "gqla_abi_version": ([], ctypes.c_int),
@@ -74,6 +97,9 @@ _SIGS = {
                          _f32p, _f32p, _f32p, _vp], ctypes.c_int),
     "gqla_splitkv_combine": ([ctypes.POINTER(Dims), ctypes.c_int32, _i32p, ctypes.c_int32,
                               _f32p, _f32p, _vp, _f32p, _vp], ctypes.c_int),
+    "gqla_select_path": ([ctypes.POINTER(Dims), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
+                          ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(Hw),
+                          ctypes.POINTER(PathEstimate), ctypes.POINTER(PathEstimate)], ctypes.c_int),
 }
 
 _lib = None
@@ -306,3 +332,15 @@ def expand_cache(d: Dims, latent_pages, w_uk, w_uv, page_ids=None, stream=None):
                     dtype=torch.bfloat16, device=latent_pages.device)
     gqla_expand_cache(d, latent_pages, w_uk, w_uv, E, page_ids=page_ids, stream=stream)
     return E
+
+
+def gqla_select_path(d: Dims, seqlens_host, s_q_absorb: int, s_q_gqa: int, hw: Hw):
+    """Roofline advisor: (chosen path, absorb estimate, GQA estimate) for one decode call of
+    each path over sequences of the given (host) lengths."""
+    lens = (ctypes.c_int32 * len(seqlens_host))(*[int(x) for x in seqlens_host])
+    ea, eg = PathEstimate(), PathEstimate()
+    st = lib().gqla_select_path(ctypes.byref(d), len(seqlens_host), lens, int(s_q_absorb),
+                                int(s_q_gqa), ctypes.byref(hw), ctypes.byref(ea), ctypes.byref(eg))
+    if st < 0:
+        raise GqlaError(st, "gqla_select_path")
+    return st, ea, eg

@@ -139,7 +139,7 @@ int enqueue_combine(const gqla_dims* d, int32_t batch, const int32_t* split_offs
 
 extern "C" {
 
-int gqla_abi_version(void) { return 200; }
+int gqla_abi_version(void) { return 201; }
 
 const char* gqla_status_string(int status) {
   switch (status) {

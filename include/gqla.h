@@ -191,6 +191,52 @@ int gqla_splitkv_combine(const gqla_dims* d, int32_t batch, const int32_t* split
                          int32_t total_splits, const float* part_out, const float* part_lse,
                          void* out, float* lse, void* stream);
 
+/* ---- Path selector (roofline advisor) ----------------------------------
+ * The pages pick the path per hardware by comparing each path's arithmetic
+ * intensity with the ridge point (paperlayer.ai section 4 "Roofline
+ * analysis" and "Hardware operating points"; gist.science section 2
+ * "Pfadauswahl"); they state no policy beyond that.  This estimates one
+ * decode call of each path over a batch with the pages' roofline model,
+ * time = max(bytes / bandwidth, FLOPs / peak), divided by the fraction of that
+ * bound the path reaches on the given hardware, and recommends the path with
+ * the higher query tokens per second (ties go to the absorb path, which needs
+ * no expanded cache).  Host-only: no device memory, no stream. */
+typedef struct {
+  double hbm_gbps;        /* memory bandwidth, GB/s (> 0) */
+  double mfma_tflops;     /* dense bf16 matrix peak, TFLOP/s (> 0) */
+  double frac_absorb;     /* fraction of its roofline the absorb path reaches, (0, 1] */
+  double frac_gqa;        /* same for the GQA path */
+  int32_t cache_only;     /* 1: count only cache bytes and attention FLOPs (the pages'
+                             step-time convention); 0: also the query, output and, on
+                             the absorb path, the weights and the two projections */
+} gqla_hw;
+
+typedef struct {
+  double bytes;           /* algorithmic bytes of the call (each operand moved once) */
+  double flops;           /* algorithmic FLOPs, 2 per multiply-accumulate */
+  double t_hbm_us;        /* bytes / bandwidth */
+  double t_mfma_us;       /* FLOPs / peak */
+  double t_roofline_us;   /* max of the two */
+  double t_expected_us;   /* t_roofline_us / frac */
+  double tokens_per_s;    /* batch * s_q / t_expected_us */
+  int32_t bound;          /* 0 = memory-bound, 1 = compute-bound */
+} gqla_path_estimate;
+
+#define GQLA_PATH_ABSORB 0
+#define GQLA_PATH_GQA 1
+
+/* Estimates of one gqla_decode_mqa_absorb call with s_q_absorb query tokens
+ * per sequence and one gqla_decode_gqa call with s_q_gqa (e.g. 1 and 2 with
+ * one MTP head), over `batch` sequences of lengths cache_seqlens_host (HOST
+ * int32 [batch], each >= the larger s_q).  d->s_q and d->block_size are not
+ * used.  Writes *absorb and *gqa (either may be NULL) and returns
+ * GQLA_PATH_ABSORB or GQLA_PATH_GQA; GQLA_ERR_INVALID_ARG for NULL d, hw or
+ * lengths, batch < 1, s_q outside [1, 2], a length below s_q, a
+ * non-positive rate or a fraction outside (0, 1]. */
+int gqla_select_path(const gqla_dims* d, int32_t batch, const int32_t* cache_seqlens_host,
+                     int32_t s_q_absorb, int32_t s_q_gqa, const gqla_hw* hw,
+                     gqla_path_estimate* absorb, gqla_path_estimate* gqa);
+
 /* Human-readable text for a status code (static storage; never NULL). */
 const char* gqla_status_string(int status);
 
