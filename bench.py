@@ -63,6 +63,8 @@ def parse():
                     help="sequences of the batch the CPU oracle decodes (bounded sample)")
     ap.add_argument("--only", choices=["absorb", "gqa"], default=None,
                     help="profiling aid: run only one path per step (not a valid bench line)")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the (g, s_q) = (4, 1) configuration measured after the main steps")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="run only a plain device copy of this many bytes (counter calibration)")
     return ap.parse_args()
@@ -103,6 +105,58 @@ def cpu_baseline(case_abs, case_gqa, n_seqs: int):
     return {"value": toks / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"fp64 numpy literal decode (expand per group, then softmax attention) of "
                       f"{n_seqs} of the 64 sequences on both paths ({toks} tokens, {dt:.1f} s)"}
+
+
+def measure_g4(G, rf, config_case, steps: int, absorb_split: int):
+    """The pages' other ridge-optimal configuration, (g, s_q) = (4, 1): 32 heads per group,
+    2176 B per token in the expanded cache; both paths over a 64 x 4096 batch, alternating
+    (each path's cache flushes the other's from the 256 MB memory-side cache)."""
+    import torch
+    case = config_case("dsv3_g4", 1)
+    d = G.Dims.of(case)
+    dev = "cuda"
+    pages, bt, sl = case.pages.to(dev), case.block_table.to(dev), case.seqlens.to(dev)
+    w_uk, w_uv = case.w_uk.to(dev), case.w_uv.to(dev)
+    qn, qr = case.q_nope.to(dev), case.q_rope.to(dev)
+    B = case.batch
+    lens = [int(x) for x in case.seqlens]
+    E = G.expand_cache(d, pages, w_uk, w_uv)
+    out = torch.empty(B, 1, case.h_q, case.d_v, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(B, 1, case.h_q, dtype=torch.float32, device=dev)
+    sa = G.make_split_plan(lens, absorb_split) + (absorb_split,) if absorb_split else None
+    ws = G.absorb_workspace(d, B, total_splits=sa[1] if sa else 0)
+    fns = {
+        "mqa_absorb": lambda: G.gqla_decode_mqa_absorb(d, qn, qr, pages, bt, sl, w_uk, w_uv, out=out, lse=lse,
+                                                       split_offsets=sa[0] if sa else None,
+                                                       split_tokens=sa[2] if sa else 0,
+                                                       total_splits=sa[1] if sa else 0, workspace=ws),
+        "gqa": lambda: G.gqla_decode_gqa(d, qn, qr, E, bt, sl, out=out, lse=lse),
+    }
+    for _ in range(3):
+        for fn in fns.values():
+            fn()
+    torch.cuda.synchronize()
+    evs = {k: [] for k in fns}
+    for _ in range(steps):
+        for k, fn in fns.items():
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            evs[k].append((a, b))
+    torch.cuda.synchronize()
+    works = {"mqa_absorb": rf.work_absorb(lens, 128, 4, 512, 64, 128, 128, 1),
+             "gqa": rf.work_gqa(lens, 128, 4, 64, 128, 128, 1)}
+    res = {}
+    for k in fns:
+        us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs[k])
+        med = us[len(us) // 2]
+        w = works[k]
+        res[k] = {"us_median": med, "tok_s": B / (med * 1e-6), "roofline_us": w.roofline_us(),
+                  "roofline_frac": w.roofline_us() / med, "bound": w.bound(), "alg_bytes": w.bytes}
+    del E
+    return {"workload": "(g, s_q) = (4, 1): 128 query heads in 4 groups of 32, latent 512 + rope 64, "
+                        "batch 64, context 4096", "paths": res}
 
 
 def main():
@@ -249,6 +303,10 @@ def main():
         selector = {"at_roofline": names[at_roof], "with_measured_fractions": names[measured],
                     "frac_absorb": fa, "frac_gqa": fg,
                     "tok_s_absorb": ea.tokens_per_s, "tok_s_gqa": eg.tokens_per_s}
+    variants = None
+    if not args.only and not args.no_variants:
+        log("(g, s_q) = (4, 1) variant")
+        variants = {"g4_sq1": measure_g4(G, rf, config_case, args.steps, args.absorb_split)}
     cpu = None
     if not args.no_cpu and not args.only:
         log("cpu oracle baseline")
@@ -269,6 +327,7 @@ def main():
         "paths": per_path,
         "expand_us": t_expand_us,
         "path_selector": selector,
+        "variants": variants,
         "kernel_source_hash": src_hash,
     }
     print(json.dumps(line))

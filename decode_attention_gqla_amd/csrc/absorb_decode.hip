@@ -502,7 +502,8 @@ void absorb_decode_kernel(DecodeParams p) {
 }
 
 // Merge of the split partials and up-projection, per (group G, block of SB
-// sequences): for each query row of the block,
+// sequences, or a 32-row chunk of one sequence's group rows when a group has
+// more than 32): for each query row of the block,
 //   m = max_s lse_s,  w_s = exp(lse_s - m),  o = sum_s w_s o_lat_s / sum_s w_s,
 //   lse = m + ln sum_s w_s,  out = o W_UV[G].
 // o is split into bf16 hi + lo (o - hi, rounded), both multiplied on the
@@ -514,7 +515,9 @@ __global__ __launch_bounds__(512) void absorb_merge_kernel(DecodeParams p) {
   constexpr int NWM = 8;                            // waves
   constexpr int RG = HPG * SQ;                      // rows of one group per sequence
   constexpr int SB = RG >= 32 ? 1 : 32 / RG;        // sequences per workgroup
-  constexpr int NR = SB * RG;                       // rows per workgroup
+  constexpr int RCH = RG > 32 ? RG / 32 : 1;        // workgroups per (sequence, group)
+  constexpr int NR = RG > 32 ? 32 : SB * RG;        // rows per workgroup
+  static_assert(RG <= 32 || RG % 32 == 0, "row chunks of 32");
   constexpr int NT = NR / 16;                       // 16-row tiles
   constexpr int STR = 2 * R + 16;                   // LDS row stride (bytes)
   constexpr int MD = DV / 16;                       // 16-dim output tiles
@@ -525,7 +528,8 @@ __global__ __launch_bounds__(512) void absorb_merge_kernel(DecodeParams p) {
   static_assert(MD <= NWM, "one output tile per wave");
   __shared__ __attribute__((aligned(16))) unsigned char sm_raw[2 * NR * STR];
   lds_u8_t* const sm = (lds_u8_t*)sm_raw;
-  const int G = blockIdx.y, b0 = blockIdx.x * SB;
+  const int G = blockIdx.y, b0 = (blockIdx.x / RCH) * SB;
+  const int lr0 = (blockIdx.x % RCH) * 32;          // first group row of this workgroup
   const int H = HPG * p.num_groups;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -549,7 +553,7 @@ __global__ __launch_bounds__(512) void absorb_merge_kernel(DecodeParams p) {
 #pragma unroll
   for (int j = 0; j < RPW; ++j) {
     const int rr = w + NWM * j;
-    const int b = b0 + rr / RG, lr = rr % RG;
+    const int b = b0 + rr / RG, lr = lr0 + rr % RG;
     const bool bv = b < p.batch;
     const int bc = bv ? b : 0;                      // loads stay in bounds, no branch
     const int o0 = p.split_offsets ? p.split_offsets[bc] : bc;
@@ -655,7 +659,7 @@ __global__ __launch_bounds__(512) void absorb_merge_kernel(DecodeParams p) {
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int rr = 16 * nt + c;
-    const int b = b0 + rr / RG, lr = rr % RG;
+    const int b = b0 + rr / RG, lr = lr0 + rr % RG;
     if (b >= p.batch) continue;
     const int h = G * HPG + lr / SQ, i = lr % SQ;
     u32x2 pk = {pack_bf16x2(oacc[nt][0], oacc[nt][1]), pack_bf16x2(oacc[nt][2], oacc[nt][3])};
@@ -797,8 +801,8 @@ hipError_t launch_absorb(const DecodeParams& p, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  constexpr int RG = HPG * SQ, SB = RG >= 32 ? 1 : 32 / RG;
-  dim3 grid((unsigned)((p.batch + SB - 1) / SB), (unsigned)p.num_groups);
+  constexpr int RG = HPG * SQ, SB = RG >= 32 ? 1 : 32 / RG, RCH = RG > 32 ? RG / 32 : 1;
+  dim3 grid((unsigned)((p.batch + SB - 1) / SB * RCH), (unsigned)p.num_groups);
   hipLaunchKernelGGL((absorb_merge_kernel<HPG, SQ, R, DV>), grid, dim3(512), 0, stream, p);
   return hipGetLastError();
 }
@@ -811,6 +815,8 @@ hipError_t absorb_dispatch(int hpg, int sq, int r, int dn, int dv, int dr, const
     return launch_absorb<HPG, SQ, R, DR, DN, DV>(p, stream);
   GQLA_ABS_CASE(16, 1, 512, 64, 128, 128)
   GQLA_ABS_CASE(16, 2, 512, 64, 128, 128)
+  GQLA_ABS_CASE(32, 1, 512, 64, 128, 128)
+  GQLA_ABS_CASE(32, 2, 512, 64, 128, 128)
   GQLA_ABS_CASE(4, 1, 512, 64, 128, 128)
   GQLA_ABS_CASE(4, 2, 512, 64, 128, 128)
   GQLA_ABS_CASE(8, 1, 64, 16, 32, 32)

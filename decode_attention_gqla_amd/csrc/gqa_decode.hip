@@ -53,7 +53,7 @@ struct GqaCfg {
   static_assert(DN % 32 == 0 && DV % 16 == 0 && DR % 8 == 0, "unsupported head dims");
   static_assert(K_BYTES % 1024 == 0 && V_BYTES % 1024 == 0, "whole DMA instructions");
   static_assert(NI % NW == 0, "the waves share the copies evenly");
-  static_assert(NW <= 2, "launch bound of 128 threads");
+  static_assert(NW <= 4, "launch bound of 256 threads");
   static_assert(LA * NIW < 64, "vmcnt budget");
   static_assert(LA <= 3, "the in-flight wait covers up to two later tiles");
   static_assert((KCH & (KCH - 1)) == 0 && (RCH & (RCH - 1)) == 0, "power-of-two rows");
@@ -70,7 +70,7 @@ __device__ __forceinline__ int rswz(int t) { return ((t >> 1) & 1) | ((t >> 3) <
 __device__ __forceinline__ int vswz(int d) { return 2 * ((d >> 2) & 1); }
 
 template <int HPG, int SQ, int DN, int DV, int DR>
-__global__ __launch_bounds__(128) void gqa_decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256) void gqa_decode_kernel(DecodeParams p) {
   using C = GqaCfg<HPG, SQ, DN, DV, DR>;
   constexpr int BS = C::BS, NW = C::NW, KSN = C::KSN, KSR = C::KSR, MT = C::MT;
   constexpr int KCH = C::KCH, RCH = C::RCH, VCH = C::VCH;
@@ -308,6 +308,8 @@ hipError_t gqa_dispatch(int hpg, int sq, int dn, int dv, int dr, const DecodePar
   if (hpg == HPG && sq == SQ && dn == DN && dv == DV && dr == DR) return launch_gqa<HPG, SQ, DN, DV, DR>(p, stream);
   GQLA_GQA_CASE(16, 1, 128, 128, 64)
   GQLA_GQA_CASE(16, 2, 128, 128, 64)
+  GQLA_GQA_CASE(32, 1, 128, 128, 64)
+  GQLA_GQA_CASE(32, 2, 128, 128, 64)
   GQLA_GQA_CASE(4, 1, 128, 128, 64)
   GQLA_GQA_CASE(4, 2, 128, 128, 64)
   GQLA_GQA_CASE(8, 1, 32, 32, 16)

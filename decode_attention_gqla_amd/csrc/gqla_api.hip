@@ -28,7 +28,7 @@ bool shape_supported(const gqla_dims* d) {
   const int hpg = d->num_heads / d->num_groups;
   if (d->block_size != 64 || (d->s_q != 1 && d->s_q != 2)) return false;
   if (d->d_latent == 512 && d->d_rope == 64 && d->d_nope == 128 && d->d_v == 128)
-    return hpg == 16 || hpg == 4;
+    return hpg == 16 || hpg == 4 || hpg == 32;
   if (d->d_latent == 64 && d->d_rope == 16 && d->d_nope == 32 && d->d_v == 32) return hpg == 8;
   return false;
 }

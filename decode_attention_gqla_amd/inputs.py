@@ -38,6 +38,9 @@ CONFIGS = {
     "dsv3":        dict(h_q=128, g=8, r=512, d_R=64, d_nope=128, d_v=128, batch=64, ctx=4096),
     "dsv3_ragged": dict(h_q=128, g=8, r=512, d_R=64, d_nope=128, d_v=128, batch=16,
                         ctx=("loguniform", 1024, 32768)),
+    # the pages' other ridge-optimal GQA configuration, (g, s_q) = (4, 1): 32 heads per
+    # group, 2176 B per token in the expanded cache
+    "dsv3_g4":     dict(h_q=128, g=4, r=512, d_R=64, d_nope=128, d_v=128, batch=64, ctx=4096),
 }
 
 
@@ -125,7 +128,7 @@ def config_case(name: str, s_q: int, *, seed=None, batch=None, ctx=None, table=N
                 poison=False, dtype=torch.bfloat16) -> Case:
     """A case shaped like one of CONFIGS (batch/ctx may be overridden for smaller runs)."""
     c = dict(CONFIGS[name])
-    base_seed = {"tiny": 1000, "llama3_8b": 1001, "dsv3": 1002, "dsv3_ragged": 1004}[name]
+    base_seed = {"tiny": 1000, "llama3_8b": 1001, "dsv3": 1002, "dsv3_ragged": 1004, "dsv3_g4": 1005}[name]
     if table is None:
         table = "random" if name == "dsv3_ragged" else "identity"
     return make_case(c["h_q"], c["g"], c["r"], c["d_R"], c["d_nope"], c["d_v"],

@@ -54,7 +54,8 @@
  * Supported shapes (compile-time instantiations; others return
  * GQLA_ERR_UNSUPPORTED_SHAPE): block_size = 64, s_q in {1, 2}, and
  *   (h_q/g, d_latent, d_rope, d_nope, d_v) in
- *     {(16, 512, 64, 128, 128), (4, 512, 64, 128, 128), (8, 64, 16, 32, 32)}.
+ *     {(16, 512, 64, 128, 128), (32, 512, 64, 128, 128), (4, 512, 64, 128, 128),
+ *      (8, 64, 16, 32, 32)}.
  */
 #ifndef GQLA_H
 #define GQLA_H

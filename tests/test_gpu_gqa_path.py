@@ -93,6 +93,8 @@ CASES = [
     ("llama3_8b", 1, dict(batch=4)), ("llama3_8b", 2, dict(batch=4)),
     ("dsv3", 2, dict(batch=3, ctx=(4096, 1000, 77))),
     ("dsv3", 1, dict(batch=2, ctx=(129, 2))),
+    ("dsv3_g4", 1, dict(batch=3, ctx=(4096, 1000, 77))),
+    ("dsv3_g4", 2, dict(batch=2, ctx=(1500, 33))),
 ]
 
 
