@@ -107,6 +107,41 @@ def cpu_baseline(case_abs, case_gqa, n_seqs: int):
                       f"{n_seqs} of the 64 sequences on both paths ({toks} tokens, {dt:.1f} s)"}
 
 
+def measure_append(G, d, pages, bt, sl, lens, w_uk, w_uv, E, steps: int, n_new: int = 2):
+    """One step's incremental append: the last n_new tokens of every sequence written into the
+    latent pages and their K/V/rope slots into the expanded cache (the rows are the ones already
+    there, so the caches do not change)."""
+    import torch
+    B = len(lens)
+    btc = bt.cpu()
+    idx = []
+    for b, L in enumerate(lens):
+        for j in range(n_new):
+            t = L - n_new + j
+            idx.append((int(btc[b, t // 64]), t % 64))
+    pg = torch.tensor([i for i, _ in idx], device="cuda")
+    sl_ = torch.tensor([s for _, s in idx], device="cuda")
+    rows = pages[pg, sl_].reshape(B, n_new, -1).contiguous()
+    fn = lambda: G.gqla_append_tokens(d, rows, pages, bt, sl, w_uk, w_uv, expanded_pages=E)
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    # back-to-back calls between two events (the host enqueues ahead, so launch overhead on the
+    # host does not show), several repeats
+    us = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        us.append(a.elapsed_time(b) * 1e3 / steps)
+    us.sort()
+    return {"workload": f"{n_new} new tokens for each of {B} sequences: latent rows plus their K, V and "
+                        "rope slots in the expanded cache (g = 8)", "us_per_call_median": us[len(us) // 2]}
+
+
 def measure_g4(G, rf, config_case, steps: int, absorb_split: int):
     """The pages' other ridge-optimal configuration, (g, s_q) = (4, 1): 32 heads per group,
     2176 B per token in the expanded cache; both paths over a 64 x 4096 batch, alternating
@@ -125,12 +160,19 @@ def measure_g4(G, rf, config_case, steps: int, absorb_split: int):
     lse = torch.empty(B, 1, case.h_q, dtype=torch.float32, device=dev)
     sa = G.make_split_plan(lens, absorb_split) + (absorb_split,) if absorb_split else None
     ws = G.absorb_workspace(d, B, total_splits=sa[1] if sa else 0)
+    # GQA: one workgroup per (sequence, group) is only 256 workgroups of two waves here, so the
+    # call is split into 2048-token partitions (512 workgroups) and merged by the combine
+    gsplit = 2048
+    og, tg = G.make_split_plan(lens, gsplit)
+    po = torch.empty(tg, 1, case.h_q, case.d_v, dtype=torch.float32, device=dev)
+    pl = torch.empty(tg, 1, case.h_q, dtype=torch.float32, device=dev)
     fns = {
         "mqa_absorb": lambda: G.gqla_decode_mqa_absorb(d, qn, qr, pages, bt, sl, w_uk, w_uv, out=out, lse=lse,
                                                        split_offsets=sa[0] if sa else None,
                                                        split_tokens=sa[2] if sa else 0,
                                                        total_splits=sa[1] if sa else 0, workspace=ws),
-        "gqa": lambda: G.gqla_decode_gqa(d, qn, qr, E, bt, sl, out=out, lse=lse),
+        "gqa": lambda: G.gqla_decode_gqa(d, qn, qr, E, bt, sl, out=out, lse=lse, split_offsets=og,
+                                         split_tokens=gsplit, total_splits=tg, part_out=po, part_lse=pl),
     }
     for _ in range(3):
         for fn in fns.values():
@@ -156,7 +198,8 @@ def measure_g4(G, rf, config_case, steps: int, absorb_split: int):
                   "roofline_frac": w.roofline_us() / med, "bound": w.bound(), "alg_bytes": w.bytes}
     del E
     return {"workload": "(g, s_q) = (4, 1): 128 query heads in 4 groups of 32, latent 512 + rope 64, "
-                        "batch 64, context 4096", "paths": res}
+                        "batch 64, context 4096", "absorb_split_tokens": absorb_split,
+            "gqa_split_tokens": gsplit, "paths": res}
 
 
 def main():
@@ -306,7 +349,8 @@ def main():
     variants = None
     if not args.only and not args.no_variants:
         log("(g, s_q) = (4, 1) variant")
-        variants = {"g4_sq1": measure_g4(G, rf, config_case, args.steps, args.absorb_split)}
+        variants = {"append_2_tokens": measure_append(G, d2, pages, bt, sl, lens, w_uk, w_uv, E, args.steps),
+                    "g4_sq1": measure_g4(G, rf, config_case, args.steps, args.absorb_split)}
     cpu = None
     if not args.no_cpu and not args.only:
         log("cpu oracle baseline")

@@ -97,6 +97,9 @@ _SIGS = {
                          _f32p, _f32p, _f32p, _vp], ctypes.c_int),
     "gqla_splitkv_combine": ([ctypes.POINTER(Dims), ctypes.c_int32, _i32p, ctypes.c_int32,
                               _f32p, _f32p, _vp, _f32p, _vp], ctypes.c_int),
+    "gqla_append_tokens": ([ctypes.POINTER(Dims), ctypes.c_int32, ctypes.c_int32, _vp, _vp,
+                            ctypes.c_int64, _i32p, ctypes.c_int32, _i32p, _vp, _vp, _vp, _vp],
+                           ctypes.c_int),
     "gqla_select_path": ([ctypes.POINTER(Dims), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
                           ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(Hw),
                           ctypes.POINTER(PathEstimate), ctypes.POINTER(PathEstimate)], ctypes.c_int),
@@ -344,3 +347,20 @@ def gqla_select_path(d: Dims, seqlens_host, s_q_absorb: int, s_q_gqa: int, hw: H
     if st < 0:
         raise GqlaError(st, "gqla_select_path")
     return st, ea, eg
+
+
+def gqla_append_tokens(d: Dims, new_rows, latent_pages, block_table, cache_seqlens, w_uk=None,
+                       w_uv=None, expanded_pages=None, stream=None) -> None:
+    """Write the new tokens' latent rows (bf16 [batch, n_new, r + d_R]) into their paged slots;
+    with expanded_pages, also their K, V and rope slots of the expanded cache."""
+    B, n_new = int(new_rows.shape[0]), int(new_rows.shape[1])
+    row = d.d_latent + d.d_rope
+    st = lib().gqla_append_tokens(
+        ctypes.byref(d), B, n_new, _ptr(new_rows, torch.bfloat16, "new_rows", (B, n_new, row)),
+        _ptr(latent_pages, torch.bfloat16, "latent_pages"), int(latent_pages.shape[0]),
+        _ptr(block_table, torch.int32, "block_table"), int(block_table.shape[1]),
+        _ptr(cache_seqlens, torch.int32, "cache_seqlens", (B,)),
+        _ptr(w_uk, torch.bfloat16, "w_uk", allow_none=True),
+        _ptr(w_uv, torch.bfloat16, "w_uv", allow_none=True),
+        _ptr(expanded_pages, torch.bfloat16, "expanded_pages", allow_none=True), _stream(stream))
+    _check(st, "gqla_append_tokens")

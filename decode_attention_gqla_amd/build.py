@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgqla.so")
-SOURCES = ["gqla_api.hip", "gqa_decode.hip", "absorb_decode.hip", "expand.hip", "combine.hip", "select.hip"]
+SOURCES = ["gqla_api.hip", "gqa_decode.hip", "absorb_decode.hip", "expand.hip", "combine.hip", "select.hip", "append.hip"]
 ARCH = "gfx950"
 
 

@@ -16,6 +16,7 @@ hipError_t absorb_dispatch(int hpg, int sq, int r, int dn, int dv, int dr, const
 hipError_t expand_dispatch(int r, int dn, int dv, int dr, const ExpandParams& p, hipStream_t stream,
                            bool* supported);
 hipError_t combine_dispatch(int dv, const CombineParams& p, hipStream_t stream, bool* supported);
+hipError_t append_launch(const AppendParams& p, int r, int dn, int dv, int dr, hipStream_t stream, bool* supported);
 }  // namespace gqla
 
 namespace {
@@ -223,6 +224,40 @@ int gqla_expand_cache(const gqla_dims* d, const void* latent_pages, const void* 
   bool ok = true;
   hipError_t e = gqla::expand_dispatch(d->d_latent, d->d_nope, d->d_v, d->d_rope, p,
                                        (hipStream_t)stream, &ok);
+  return finish(e, ok);
+}
+
+int gqla_append_tokens(const gqla_dims* d, int32_t batch, int32_t n_new, const void* new_rows,
+                       void* latent_pages, int64_t num_pages, const int32_t* block_table,
+                       int32_t max_blocks, const int32_t* cache_seqlens, const void* w_uk,
+                       const void* w_uv, void* expanded_pages, void* stream) {
+  int st = check_dims(d);
+  if (st != GQLA_OK) return st;
+  if (batch < 1 || n_new < 1 || n_new > d->block_size || num_pages < 1 || max_blocks < 1)
+    return GQLA_ERR_INVALID_ARG;
+  if (!new_rows || !latent_pages || !block_table || !cache_seqlens) return GQLA_ERR_INVALID_ARG;
+  if (expanded_pages && (!w_uk || !w_uv)) return GQLA_ERR_INVALID_ARG;
+  if (!aligned16(new_rows) || !aligned16(latent_pages) || !aligned4(block_table) ||
+      !aligned4(cache_seqlens) ||
+      (expanded_pages && (!aligned16(expanded_pages) || !aligned16(w_uk) || !aligned16(w_uv))))
+    return GQLA_ERR_MISALIGNED;
+  gqla::AppendParams a;
+  a.new_rows = (const uint16_t*)new_rows;
+  a.latent = (uint16_t*)latent_pages;
+  a.block_table = block_table;
+  a.seqlens = cache_seqlens;
+  a.w_uk = (const uint16_t*)w_uk;
+  a.w_uv = (const uint16_t*)w_uv;
+  a.expanded = (uint16_t*)expanded_pages;
+  a.row_elems = (int64_t)d->d_latent + d->d_rope;
+  a.num_groups = d->num_groups;
+  a.batch = batch;
+  a.n_new = n_new;
+  a.max_blocks = max_blocks;
+  a.bs = d->block_size;
+  (void)num_pages;
+  bool ok = true;
+  hipError_t e = gqla::append_launch(a, d->d_latent, d->d_nope, d->d_v, d->d_rope, (hipStream_t)stream, &ok);
   return finish(e, ok);
 }
 

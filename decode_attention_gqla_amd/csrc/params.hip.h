@@ -39,6 +39,22 @@ struct ExpandParams {
   int32_t num_groups;
 };
 
+struct AppendParams {
+  const uint16_t* new_rows;      // [batch][n_new][row_elems]
+  uint16_t* latent;              // [n_pages][bs][row_elems]
+  const int32_t* block_table;    // [batch][max_blocks]
+  const int32_t* seqlens;        // [batch], counting the new tokens
+  const uint16_t* w_uk;          // [g][r][d_nope]  (with expanded)
+  const uint16_t* w_uv;          // [g][r][d_v]     (with expanded)
+  uint16_t* expanded;            // [n_pages][page_elems], or nullptr (latent only)
+  int64_t row_elems;             // r + d_rope
+  int32_t num_groups;
+  int32_t batch;
+  int32_t n_new;
+  int32_t max_blocks;
+  int32_t bs;
+};
+
 struct CombineParams {
   const float* part_out;         // [S][rows][d_v]
   const float* part_lse;         // [S][rows]

@@ -116,6 +116,28 @@ int gqla_expand_cache(const gqla_dims* d, const void* latent_pages, const void* 
                       const void* w_uv, int64_t num_pages, const int32_t* page_ids,
                       int64_t num_pages_to_expand, void* expanded_pages, void* stream);
 
+/* Incremental append (the step beside decode that live serving needs): after
+ * the one-shot conversion the latent pages stay the stored state and the GQA
+ * path decodes with no per-step latent expansion (paperlayer.ai section 4
+ * "GQA path"), but each step's new tokens still need their latent rows and,
+ * for the GQA path, their per-group K/V.
+ *   new_rows  bf16 [batch][n_new][d_latent + d_rope]: the new tokens' c ++ k_rope,
+ *             written to positions cache_seqlens[b] - n_new .. cache_seqlens[b] - 1
+ *             of sequence b (cache_seqlens counts the new tokens, as the decode
+ *             calls take it; 1 <= n_new <= block_size <= cache_seqlens[b]);
+ *   latent_pages, num_pages, block_table, max_blocks: as for the decode calls;
+ *   expanded_pages  NULL, or the expanded cache: then the new tokens' K, V and
+ *             rope slots are written too (w_uk and w_uv required), computed
+ *             exactly as gqla_expand_cache computes them, so the expanded cache
+ *             stays bit-identical to a full expansion of the latent cache; no
+ *             other slot is written.
+ * The latent rows are written before the expansion reads them (one stream).
+ * Two new tokens must not share a slot. */
+int gqla_append_tokens(const gqla_dims* d, int32_t batch, int32_t n_new, const void* new_rows,
+                       void* latent_pages, int64_t num_pages, const int32_t* block_table,
+                       int32_t max_blocks, const int32_t* cache_seqlens, const void* w_uk,
+                       const void* w_uv, void* expanded_pages, void* stream);
+
 /* MQA-absorb decode over the latent cache (paperlayer.ai section 4,
  * "MQA-absorb path"; gist.science section 2 "MQA-Absorb-Pfad"):
  *   q_abs = W_UK[G] q_nope,  s_t = (q_abs . c_t + q_rope . k_rope_t) * scale,

@@ -148,6 +148,24 @@ def test_expand_and_combine_argument_errors(lib):
     assert lib.gqla_splitkv_combine(ctypes.byref(d), -1, A, 0, A, A, A, None, None) == INVALID
 
 
+def test_append_argument_errors(lib):
+    d = Dims.make(128, 8, 512, 64, 128, 128, 1)
+    fn = lib.gqla_append_tokens
+    # d, batch, n_new, rows, latent, num_pages, table, max_blocks, lens, w_uk, w_uv, expanded, stream
+    # every call below fails its argument checks on the host, before any launch
+    assert fn(ctypes.byref(d), 0, 1, A, A, 8, A, 4, A, None, None, None, None) == INVALID
+    assert fn(ctypes.byref(d), 2, 0, A, A, 8, A, 4, A, None, None, None, None) == INVALID
+    assert fn(ctypes.byref(d), 2, 65, A, A, 8, A, 4, A, None, None, None, None) == INVALID
+    assert fn(ctypes.byref(d), 2, 1, A, A, 0, A, 4, A, None, None, None, None) == INVALID
+    assert fn(ctypes.byref(d), 2, 1, None, A, 8, A, 4, A, None, None, None, None) == INVALID
+    assert fn(ctypes.byref(d), 2, 1, A, A, 8, A, 4, A, None, None, A, None) == INVALID   # weights needed
+    assert fn(ctypes.byref(d), 2, 1, A, A, 8, A, 4, A, A, ODD, A, None) == MISALIGNED
+    assert fn(ctypes.byref(d), 2, 1, ODD, A, 8, A, 4, A, None, None, None, None) == MISALIGNED
+    assert fn(None, 2, 1, A, A, 8, A, 4, A, None, None, None, None) == INVALID
+    assert fn(ctypes.byref(Dims.make(96, 8, 512, 64, 128, 128, 1)), 2, 1, A, A, 8, A, 4, A,
+              None, None, None, None) == UNSUPPORTED
+
+
 def test_binding_rejects_cpu_tensors_and_wrong_dtypes(lib):
     d = Dims.make(16, 2, 64, 16, 32, 32, 1)
     q = torch.zeros(1, 1, 16, 32, dtype=torch.bfloat16)

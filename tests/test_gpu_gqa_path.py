@@ -184,3 +184,54 @@ def test_combine_matches_oracle_on_the_same_partials(empty_frac):
     assert np.max(np.abs(got_l[full] - ref_l[full])) < 1e-4
     assert np.array_equal(got_l[~full], ref_l[~full])            # all-empty rows: -inf
     assert np.all(got_o[~full] == 0)
+
+
+# --- incremental append ---------------------------------------------------------------
+@pytest.mark.parametrize("n_new", [1, 2])
+@pytest.mark.parametrize("name", ["tiny", "dsv3"])
+def test_append_then_both_caches_equal_a_full_build(name, n_new):
+    """Appending each sequence's last n_new tokens to a cache that lacks them gives, bit for
+    bit, the latent pages of the full case and the full expansion of those pages, and writes
+    nothing else (the new tokens of the 65-token sequence straddle a page boundary when
+    n_new = 2)."""
+    log(f"append {name} n_new={n_new}")
+    ctx = (65, 300, 64, 128) if name == "tiny" else (65, 4096, 1000, 129)
+    case = config_case(name, 1, batch=4, ctx=ctx, poison=True, table="random")
+    d = dims_of_gpu(case)
+    dev = "cuda"
+    full = case.pages.to(dev)
+    bt, sl = case.block_table.to(dev), case.seqlens.to(dev)
+    w_uk, w_uv = case.w_uk.to(dev), case.w_uv.to(dev)
+    E_full = G.expand_cache(d, full, w_uk, w_uv)
+    # the state before the step: new-token slots hold something else
+    start = full.clone()
+    rows = []
+    for b in range(case.batch):
+        L = int(case.seqlens[b])
+        r_b = []
+        for j in range(n_new):
+            t = L - n_new + j
+            pg, slot = int(case.block_table[b, t // case.bs]), t % case.bs
+            r_b.append(full[pg, slot].clone())
+            start[pg, slot] = 3.0
+        rows.append(torch.stack(r_b))
+    new_rows = torch.stack(rows).contiguous()
+    E = G.expand_cache(d, start, w_uk, w_uv)
+    G.gqla_append_tokens(d, new_rows, start, bt, sl, w_uk, w_uv, expanded_pages=E)
+    torch.cuda.synchronize()
+    assert torch.equal(start.view(torch.int16), full.view(torch.int16))
+    assert torch.equal(E.view(torch.int16), E_full.view(torch.int16))
+    # latent-only append (the absorb path's cache)
+    start2 = full.clone()
+    for b in range(case.batch):
+        L = int(case.seqlens[b])
+        for j in range(n_new):
+            t = L - n_new + j
+            start2[int(case.block_table[b, t // case.bs]), t % case.bs] = -5.0
+    G.gqla_append_tokens(d, new_rows, start2, bt, sl)
+    torch.cuda.synchronize()
+    assert torch.equal(start2.view(torch.int16), full.view(torch.int16))
+
+
+def dims_of_gpu(case):
+    return G.Dims.of(case)
