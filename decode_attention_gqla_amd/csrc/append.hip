@@ -16,7 +16,7 @@
 // read from the caller's buffer, so nothing orders the copy before the
 // products.  It multiplies exactly as the one-shot
 // expansion kernel does for those tokens -- the same 16x16x32 MFMA in the same
-// orientation (K^T = W^T C^T, V = C W), the same 32-row k steps in the same
+// orientation (K^T = W_UK^T C^T, V^T = W_UV^T C^T), the same 32-row k steps in the same
 // order, the same rounding -- so every written value is bit-identical to a
 // full expansion of the updated pages; only the new tokens' slots are
 // written.
@@ -99,50 +99,33 @@ __global__ __launch_bounds__(256) void expand_tokens_kernel(AppendParams p) {
       s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)a0);
       s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)a1);
       const bf16x8 wt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      acc[m] = kind_v ? mfma16(cb[ks], wt, acc[m]) : mfma16(wt, cb[ks], acc[m]);
+      acc[m] = mfma16(wt, cb[ks], acc[m]);
     }
   }
 
   const size_t page_elems = (size_t)BS * (g * 2 * DH + DR);
   const int d0 = hsel * DC;                       // first output dim of this workgroup
-  if (!kind_v) {
-    // lane (q, c) holds dims d0 + 16 mt + 4 q .. +3 of token c
-    if (tile * 16 + c < n_tok) {
-      int page_c, slot_c;
-      locate(tok_c, page_c, slot_c);
-      uint16_t* krow = p.expanded + (size_t)page_c * page_elems + (size_t)G * BS * 2 * DH + (size_t)slot_c * DH + d0;
+  // lane (q, c) holds dims d0 + 16 mt + 4 q .. +3 of token c (K and V token-major)
+  if (tile * 16 + c < n_tok) {
+    int page_c, slot_c;
+    locate(tok_c, page_c, slot_c);
+    uint16_t* orow = p.expanded + (size_t)page_c * page_elems + (size_t)G * BS * 2 * DH + (kind_v ? BS * DH : 0) +
+                     (size_t)slot_c * DH + d0;
 #pragma unroll
-      for (int m = 0; m < MTW; ++m) {
-        const int mt = w * MTW + m;
-        if (mt >= MTC) break;
-        u32x2 pk = {pack_bf16x2(acc[m][0], acc[m][1]), pack_bf16x2(acc[m][2], acc[m][3])};
-        *reinterpret_cast<u32x2*>(krow + 16 * mt + 4 * q) = pk;
-      }
-      if (G == 0 && hsel == 0 && w == 0) {        // the token's latent row and shared rope key
-        uint16_t* rope = p.expanded + (size_t)page_c * page_elems + (size_t)g * BS * 2 * DH + (size_t)slot_c * DR;
-        const uint16_t* src = p.new_rows + (size_t)tok_c * ROW;
-        uint16_t* lat = p.latent + ((size_t)page_c * BS + slot_c) * ROW;
-        for (int part = q; part < DR / 8; part += 4)
-          *reinterpret_cast<u32x4*>(rope + 8 * part) = *reinterpret_cast<const u32x4*>(src + R + 8 * part);
-        for (int part = q; part < ROW / 8; part += 4)
-          *reinterpret_cast<u32x4*>(lat + 8 * part) = *reinterpret_cast<const u32x4*>(src + 8 * part);
-      }
+    for (int m = 0; m < MTW; ++m) {
+      const int mt = w * MTW + m;
+      if (mt >= MTC) break;
+      u32x2 pk = {pack_bf16x2(acc[m][0], acc[m][1]), pack_bf16x2(acc[m][2], acc[m][3])};
+      *reinterpret_cast<u32x2*>(orow + 16 * mt + 4 * q) = pk;
     }
-  } else {
-    // lane (q, c) holds tokens 4 q .. 4 q + 3 of dim d0 + 16 mt + c (V^T is dim-major)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tok = tile * 16 + 4 * q + i;
-      if (tok >= n_tok) break;
-      int page, slot;
-      locate(tok, page, slot);
-      uint16_t* vblk = p.expanded + (size_t)page * page_elems + (size_t)G * BS * 2 * DH + BS * DH;
-#pragma unroll
-      for (int m = 0; m < MTW; ++m) {
-        const int mt = w * MTW + m;
-        if (mt >= MTC) break;
-        vblk[(size_t)(d0 + 16 * mt + c) * BS + slot] = (uint16_t)(pack_bf16x2(acc[m][i], 0.f) & 0xffffu);
-      }
+    if (G == 0 && !kind_v && hsel == 0 && w == 0) {   // the token's latent row and shared rope key
+      uint16_t* rope = p.expanded + (size_t)page_c * page_elems + (size_t)g * BS * 2 * DH + (size_t)slot_c * DR;
+      const uint16_t* src = p.new_rows + (size_t)tok_c * ROW;
+      uint16_t* lat = p.latent + ((size_t)page_c * BS + slot_c) * ROW;
+      for (int part = q; part < DR / 8; part += 4)
+        *reinterpret_cast<u32x4*>(rope + 8 * part) = *reinterpret_cast<const u32x4*>(src + R + 8 * part);
+      for (int part = q; part < ROW / 8; part += 4)
+        *reinterpret_cast<u32x4*>(lat + 8 * part) = *reinterpret_cast<const u32x4*>(src + 8 * part);
     }
   }
 }

@@ -9,11 +9,11 @@
 // Each workgroup (4 waves) computes one (group, K-or-V) product for 4 pages
 // (256 tokens): a [256 x r] x [r x d] GEMM on bf16 MFMA with fp32
 // accumulation.  The weight slice for a 32-row k step is staged in LDS and
-// read with ds_read_b64_tr_b16 (transposing read), because both MFMA
-// orientations need 8 consecutive latent rows of one weight column per lane;
-// the latent rows come straight from HBM as 16-byte operand loads.  K is
-// produced as K^T = W^T C^T and V as V = C W, so every lane writes 4
-// consecutive bf16 of its output row (K token-major, V dim-major).
+// read with ds_read_b64_tr_b16 (transposing read), because the MFMA A
+// operand needs 8 consecutive latent rows of one weight column per lane; the
+// latent rows come straight from HBM as 16-byte operand loads.  Both K and V
+// are produced transposed, K^T = W_UK^T C^T and V^T = W_UV^T C^T, so every
+// lane writes 4 consecutive dims of one token (both blocks token-major).
 #include "common.hip.h"
 #include "params.hip.h"
 
@@ -115,10 +115,7 @@ __device__ __forceinline__ void expand_body(const ExpandParams& p, int64_t tile,
       s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)a1);
       bf16x8 wt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        if constexpr (kind_v) acc[mt][nt] = mfma16(cb[cur][nt], wt, acc[mt][nt]);
-        else acc[mt][nt] = mfma16(wt, cb[cur][nt], acc[mt][nt]);
-      }
+      for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma16(wt, cb[cur][nt], acc[mt][nt]);
     }
   }
 
@@ -131,13 +128,8 @@ __device__ __forceinline__ void expand_body(const ExpandParams& p, int64_t tile,
     for (int nt = 0; nt < NT; ++nt) {
       const f32x4 v = acc[mt][nt];
       u32x2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-      if constexpr (kind_v) {
-        // lane holds slots 16nt + 4q .. +3 of dim 16mt + c
-        *reinterpret_cast<u32x2*>(vblk + (16 * mt + c) * BS + 16 * nt + 4 * q) = pk;
-      } else {
-        // lane holds dims 16mt + 4q .. +3 of slot 16nt + c
-        *reinterpret_cast<u32x2*>(kblk + (16 * nt + c) * DH + 16 * mt + 4 * q) = pk;
-      }
+      // lane holds dims 16mt + 4q .. +3 of slot 16nt + c
+      *reinterpret_cast<u32x2*>((kind_v ? vblk : kblk) + (16 * nt + c) * DH + 16 * mt + 4 * q) = pk;
     }
   if (G == 0 && !kind_v) {
     uint16_t* rope = dst + (size_t)g * BS * 2 * DH;

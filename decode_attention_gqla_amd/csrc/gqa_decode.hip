@@ -7,8 +7,8 @@
 //
 // Work decomposition: one workgroup per (split unit, group), one wave per
 // 16-row tile of the group's query rows (h_q/g heads x s_q tokens, padded),
-// which stay in registers.  Each 32-token tile of the group's K block,
-// dim-major V block and the shared rope key is copied HBM -> LDS by direct
+// which stay in registers.  Each 32-token tile of the group's K and V blocks
+// (both token-major) and of the shared rope key is copied HBM -> LDS by direct
 // DMA (global_load_lds_dwordx4, three tiles ahead, no VGPR staging; the waves
 // share the copy instructions and the tile), then read as bf16 MFMA operands
 // (the copies are waited for explicitly with vmcnt, see dma16):
@@ -16,9 +16,10 @@
 //   O^T[dim][row]  += V^T[dim][token] . P^T[token][row]
 // The token order inside a tile is relabelled so that the S^T accumulator lane
 // layout is exactly the P^T B-operand layout of the PV product (lane group q
-// holds tokens 8q..8q+7), and V^T is stored dim-major, so no operand needs a
-// transpose.  The LDS copies are XOR-swizzled in 16-byte chunks so every
-// operand read is bank-conflict free.
+// holds tokens 8q..8q+7); the V^T A operand (8 tokens of one dim per lane) is
+// read from the token-major V rows with ds_read_b64_tr_b16.  The LDS copies
+// are XOR-swizzled in 16-byte chunks so every operand read is bank-conflict
+// free.
 #include <type_traits>
 
 #include "common.hip.h"
@@ -40,7 +41,7 @@ struct GqaCfg {
   static constexpr int MT = DV / 16;              // 16-dim output tiles
   static constexpr int KCH = DN / 8;              // 16-byte chunks per K row
   static constexpr int RCH = DR / 8;              // 16-byte chunks per rope row
-  static constexpr int VCH = TILE / 8;            // 16-byte chunks per V^T row (4)
+  static constexpr int VCH = DV / 8;              // 16-byte chunks per V row
   static constexpr int K_BYTES = TILE * DN * 2;
   static constexpr int V_BYTES = DV * TILE * 2;
   static constexpr int R_BYTES = TILE * DR * 2;
@@ -57,17 +58,25 @@ struct GqaCfg {
   static_assert(LA * NIW < 64, "vmcnt budget");
   static_assert(LA <= 3, "the in-flight wait covers up to two later tiles");
   static_assert((KCH & (KCH - 1)) == 0 && (RCH & (RCH - 1)) == 0, "power-of-two rows");
+  static_assert(DV == 32 || DV == 64 || DV == 128, "V rows of 64, 128 or 256 bytes");
 };
 
 // Token swizzles (tile-local token t in 0..31).  The QK reads touch 16 tokens
 // {8a + 4st + b} (a, b in 0..3) at one chunk: kswz is distinct over them.
 __device__ __forceinline__ int kswz(int t) { return (t & 3) | ((t >> 3) << 2); }
 __device__ __forceinline__ int rswz(int t) { return ((t >> 1) & 1) | ((t >> 3) << 1); }
-// V^T rows d (64 bytes): a 16-byte read is served in four passes of 16 lanes
-// (per half wave, the 4-lane quads of even and of odd bit parity) over 64
-// four-byte banks; XOR-ing chunk bit 1 with row bit 2 makes every pass of the
-// PV reads (16 rows, chunks q) hit 64 distinct banks.
-__device__ __forceinline__ int vswz(int d) { return 2 * ((d >> 2) & 1); }
+// V rows (token-major, DV dims): a transposing 8-byte read is served in two
+// passes of 32 lanes over 64 four-byte banks.  One pass of a PV read touches
+// tokens 8q + 4h + r (q of one parity, r in 0..3) at the chunk pair of its
+// 16-dim output tile.  128 / DV rows share a bank period, which separates the
+// low bits of r; the remaining bits of r and the parity of q select the chunk
+// pair, so every pass hits 64 distinct banks.  The swizzle is even: a pair
+// of chunks stays adjacent.
+template <int DV>
+__device__ __forceinline__ int vswz(int t) {
+  constexpr int LRP = DV == 128 ? 0 : (DV == 64 ? 1 : 2);   // log2 rows per bank period
+  return 2 * (((t & 3) >> LRP) | (((t >> 3) & 1) << (2 - LRP)));
+}
 
 template <int HPG, int SQ, int DN, int DV, int DR>
 __global__ __launch_bounds__(256) void gqa_decode_kernel(DecodeParams p) {
@@ -114,9 +123,9 @@ __global__ __launch_bounds__(256) void gqa_decode_kernel(DecodeParams p) {
     const uint16_t* page = p.cache + (size_t)sload_i32(bt + t0 / BS) * page_elems;
     const int slot0 = t0 % BS;
     const uint16_t* kblk = page + (size_t)G * BS * (DN + DV) + slot0 * DN;
-    const uint16_t* vblk = page + (size_t)G * BS * (DN + DV) + BS * DN + slot0;
+    const uint16_t* vblk = page + (size_t)G * BS * (DN + DV) + BS * DN + slot0 * DV;
     const uint16_t* rope = page + (size_t)g * BS * (DN + DV) + slot0 * DR;
-    // copy instruction j of the tile (K, then V^T, then rope) is issued by
+    // copy instruction j of the tile (K, then V, then rope) is issued by
     // wave j % NW
 #pragma unroll
     for (int i = 0; i < C::NI_K; ++i) {        // K rows: token-major, chunk swizzled
@@ -126,11 +135,11 @@ __global__ __launch_bounds__(256) void gqa_decode_kernel(DecodeParams p) {
       dma16(kblk, (uint32_t)(t * DN + ch * 8) * 2u, dst + i * 1024);
     }
 #pragma unroll
-    for (int i = 0; i < C::NI_V; ++i) {        // V^T rows: 32 tokens of one dim
+    for (int i = 0; i < C::NI_V; ++i) {        // V rows: token-major, chunk swizzled
       if ((C::NI_K + i) % NW != w) continue;
-      const int P = i * 64 + lane, d = P / VCH, pos = P % VCH;
-      const int ch = pos ^ vswz(d);
-      dma16(vblk, (uint32_t)(d * BS + ch * 8) * 2u, dst + C::K_BYTES + i * 1024);
+      const int P = i * 64 + lane, t = P / VCH, pos = P % VCH;
+      const int ch = pos ^ vswz<DV>(t);
+      dma16(vblk, (uint32_t)(t * DV + ch * 8) * 2u, dst + C::K_BYTES + i * 1024);
     }
 #pragma unroll
     for (int i = 0; i < C::NI_R; ++i) {        // rope rows: token-major, chunk swizzled
@@ -235,11 +244,19 @@ __global__ __launch_bounds__(256) void gqa_decode_kernel(DecodeParams p) {
       pb = __builtin_bit_cast(bf16x8, pk);
     }
     const int keep = EDGE ? min(max(L - (t0 + 8 * q), 0), 8) : 8;
+    // transposing reads: source lane (q, c) of read h addresses dims
+    // 16 mt + 4 (c & 3) .. +3 of token 8 q + 4 h + c / 4, so lane (q, c)
+    // receives dim 16 mt + c of tokens 8 q + 4 h .. +3
+    const int tv0 = 8 * q + (c >> 2), tv1 = tv0 + 4;
+    const lds_u8_t* vr0 = buf + C::K_BYTES + tv0 * (DV * 2) + 8 * (c & 1);
+    const lds_u8_t* vr1 = buf + C::K_BYTES + tv1 * (DV * 2) + 8 * (c & 1);
+    const int sw0 = vswz<DV>(tv0), sw1 = vswz<DV>(tv1);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const int d = 16 * mt + c;
-      const int pos = q ^ vswz(d);
-      bf16x8 v = __builtin_bit_cast(bf16x8, *(const lds_u32x4_t*)(buf + C::K_BYTES + (d * VCH + pos) * 16));
+      const int lch = 2 * mt + ((c >> 1) & 1);          // logical 16-byte chunk
+      s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vr0 + (lch ^ sw0) * 16));
+      s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vr1 + (lch ^ sw1) * 16));
+      bf16x8 v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       if constexpr (EDGE) v = keep_first(v, keep);
       o[mt] = mfma16(v, pb, o[mt]);
     }

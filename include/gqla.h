@@ -93,7 +93,8 @@ typedef struct gqla_dims {
  *                576 elements = 1152 B per token for the DeepSeek-V3 shape,
  *                paperlayer.ai section 5 "Conversion setup").
  * Expanded page: for G in 0..g-1: K block [block_size][d_nope] then V block
- *                [d_v][block_size] (dim-major); then rope [block_size][d_rope].
+ *                [block_size][d_v] (both token-major); then rope
+ *                [block_size][d_rope].
  *                2*g*d_h + d_rope elements per token (same passage; 4224 B per
  *                token at g = 8, section 4 "GQA path"). */
 int64_t gqla_latent_page_elems(const gqla_dims* d);

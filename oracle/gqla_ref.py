@@ -173,10 +173,11 @@ def decode_absorb_form(q_nope, q_rope, pages, block_table, seqlens, w_uk, w_uv, 
 # Expanded (per-group) cache.  The pages fix only its size, 2*g*d_h + d_R
 # elements per token (paperlayer.ai section 5, "Conversion setup").  Our page
 # layout, for one page of bs slots:
-#   for G in 0..g-1:  K block  [bs slots][d_nope]   (row-major, token-major)
-#                     V block  [d_v][bs slots]      (dim-major: each dim's
-#                                                    bs values are contiguous)
+#   for G in 0..g-1:  K block  [bs slots][d_nope]   (token-major)
+#                     V block  [bs slots][d_v]      (token-major)
 #   then              rope     [bs slots][d_R]
+# (every per-token row is contiguous, so a decode over a per-group token
+# subset gathers whole rows)
 # so a page holds bs*(g*(d_nope+d_v) + d_R) elements.
 # ---------------------------------------------------------------------------
 def expanded_page_elems(d: Dims) -> int:
@@ -188,7 +189,7 @@ def expanded_offset_k(d: Dims, G: int, slot: int, j: int) -> int:
 
 
 def expanded_offset_v(d: Dims, G: int, slot: int, j: int) -> int:
-    return G * d.bs * (d.d_nope + d.d_v) + d.bs * d.d_nope + j * d.bs + slot
+    return G * d.bs * (d.d_nope + d.d_v) + d.bs * d.d_nope + slot * d.d_v + j
 
 
 def expanded_offset_rope(d: Dims, slot: int, j: int) -> int:
@@ -214,16 +215,16 @@ def expand_pages(pages, w_uk, w_uv, d: Dims, page_ids=None) -> np.ndarray:
         for G in range(d.g):
             k_view, v_view = _expanded_group_views(out[pi], d, G)
             k_view[...] = bf16_round(C @ w_uk[G])        # [slot][j]
-            v_view[...] = bf16_round(C @ w_uv[G]).T      # [j][slot]
+            v_view[...] = bf16_round(C @ w_uv[G])        # [slot][j]
         _expanded_rope_view(out[pi], d)[...] = KR
     return out
 
 
 def _expanded_group_views(page: np.ndarray, d: Dims, G: int):
-    """Views of one page's group-G blocks: K as [slot][j], V as [j][slot]."""
+    """Views of one page's group-G blocks: K as [slot][j], V as [slot][j]."""
     base = G * d.bs * (d.d_nope + d.d_v)
     k_view = page[base: base + d.bs * d.d_nope].reshape(d.bs, d.d_nope)
-    v_view = page[base + d.bs * d.d_nope: base + d.bs * (d.d_nope + d.d_v)].reshape(d.d_v, d.bs)
+    v_view = page[base + d.bs * d.d_nope: base + d.bs * (d.d_nope + d.d_v)].reshape(d.bs, d.d_v)
     return k_view, v_view
 
 
@@ -254,7 +255,7 @@ def decode_gqa_expanded(q_nope, q_rope, expanded_pages, block_table, seqlens, d:
                 slot = t % d.bs
                 k_view, v_view = _expanded_group_views(page, d, G)
                 K[t] = k_view[slot]
-                V[t] = v_view[:, slot]
+                V[t] = v_view[slot]
                 KR[t] = _expanded_rope_view(page, d)[slot]
             for h in range(G * d.heads_per_group, (G + 1) * d.heads_per_group):
                 for i in range(d.s_q):

@@ -331,7 +331,7 @@ def test_expanded_layout_views_match_offset_definitions():
             for j in range(d.d_nope):
                 assert kv[s, j] == expanded_offset_k(d, G, s, j)
             for j in range(d.d_v):
-                assert vv[j, s] == expanded_offset_v(d, G, s, j)
+                assert vv[s, j] == expanded_offset_v(d, G, s, j)
     rv = _expanded_rope_view(page, d)
     for s in range(d.bs):
         for j in range(d.d_R):
@@ -388,7 +388,7 @@ def test_gqa_over_expanded_cache_equals_literal_up_to_bf16_storage(s_q):
         for G in range(d.g):
             kv, vv = _expanded_group_views(E_exact[p], d, G)
             kv[...] = pages[p, :, : d.r] @ w_uk[G]
-            vv[...] = (pages[p, :, : d.r] @ w_uv[G]).T
+            vv[...] = pages[p, :, : d.r] @ w_uv[G]
         _expanded_rope_view(E_exact[p], d)[...] = pages[p, :, d.r:]
     o_x, l_x = decode_gqa_expanded(q_nope, q_rope, E_exact, bt, sl, d)
     assert rel(o_x, o_l) < 1e-12 and np.max(np.abs(l_x - l_l)) < 1e-12
