@@ -152,3 +152,35 @@ def random_partials(n_splits_per_seq, s_q, h_q, d_v, seed, empty_frac=0.0):
         part_lse[mask] = float("-inf")
         part_out[mask] = 0.0
     return part_out, part_lse, torch.tensor(offsets, dtype=torch.int32)
+
+
+def sparse_indices(seqlens, g, topk, seed, *, invalid_frac=0.0, dup_frac=0.0):
+    """Per-group token selections for the sparse decode: int32 [batch][g][topk].
+
+    Recipe: for each (sequence b, group G), independently, min(topk, L_b)
+    distinct positions drawn uniformly from [0, L_b) in random order (a
+    stand-in for an indexer's top-k, which the pages leave open); slots past
+    L_b are -1.  With ``invalid_frac`` that share of the entries is replaced by
+    -1 or by a position at or past L_b, and with ``dup_frac`` that share by a
+    copy of another entry of the same list.
+    """
+    gen = torch.Generator().manual_seed(seed)
+    batch = len(seqlens)
+    idx = torch.full((batch, g, topk), -1, dtype=torch.int32)
+    for b in range(batch):
+        L = int(seqlens[b])
+        n = min(topk, L)
+        for G in range(g):
+            if n > 0:
+                idx[b, G, :n] = torch.randperm(L, generator=gen)[:n].to(torch.int32)
+            if dup_frac > 0 and n > 1:
+                m = torch.rand(topk, generator=gen) < dup_frac
+                src = torch.randint(0, n, (topk,), generator=gen)
+                idx[b, G][m] = idx[b, G][src[m]]
+            if invalid_frac > 0:
+                m = torch.rand(topk, generator=gen) < invalid_frac
+                bad = torch.where(torch.rand(topk, generator=gen) < 0.5,
+                                  torch.full((topk,), -1),
+                                  L + torch.randint(0, 1 << 20, (topk,), generator=gen))
+                idx[b, G][m] = bad[m].to(torch.int32)
+    return idx

@@ -266,6 +266,55 @@ def decode_gqa_expanded(q_nope, q_rope, expanded_pages, block_table, seqlens, d:
 
 
 # ---------------------------------------------------------------------------
+# Sparse GQLA on the GQA path (gist.science section 2, subsection "Sparse
+# GQLA"; pwwt.cn section 5 on the sparse extension; ai-feeds.com "Methods",
+# the optional sparse extension).  Each KV group attends to its own subset of
+# the cached tokens, and the subset is shared by every query head of the
+# group, which is what keeps a group's h_q/g heads a dense matrix tile.  The
+# pages leave open how the subset is chosen (an indexer such as DSA or HISA
+# picks it); here it is an input: indices[b][G] lists token positions of
+# sequence b.  Readings (each listed in the design notes):
+# * the list is shared by the s_q query rows of the step as well; row i still
+#   sees only positions t <= L - s_q + i (the causal MTP mask);
+# * entries outside [0, L) (e.g. -1 padding) are ignored;
+# * every remaining entry is one attention term, in list order, so an entry
+#   listed twice counts twice;
+# * a row that sees no entry gets out = 0 and lse = -inf.
+# ---------------------------------------------------------------------------
+def decode_gqa_sparse(q_nope, q_rope, expanded_pages, block_table, seqlens, indices, d: Dims,
+                      seqs=None):
+    """Sparse GQA decode over a stored expanded cache: softmax over the listed tokens only."""
+    q_nope, q_rope, E = map(_f64, (q_nope, q_rope, expanded_pages))
+    indices = np.asarray(indices)
+    seqs = range(q_nope.shape[0]) if seqs is None else list(seqs)
+    out = np.zeros((len(seqs), d.s_q, d.h_q, d.d_v))
+    lse = np.full((len(seqs), d.s_q, d.h_q), -np.inf)
+    for bi, b in enumerate(seqs):
+        L = int(seqlens[b])
+        for G in range(d.g):
+            sel = [int(t) for t in indices[b][G] if 0 <= int(t) < L]
+            n = len(sel)
+            K = np.empty((n, d.d_nope))
+            V = np.empty((n, d.d_v))
+            KR = np.empty((n, d.d_R))
+            for e, t in enumerate(sel):
+                page = E[int(block_table[b][t // d.bs])]
+                slot = t % d.bs
+                k_view, v_view = _expanded_group_views(page, d, G)
+                K[e] = k_view[slot]
+                V[e] = v_view[slot]
+                KR[e] = _expanded_rope_view(page, d)[slot]
+            for i in range(d.s_q):
+                vis = np.array([t < visible_tokens(L, i, d.s_q) for t in sel], dtype=bool)
+                if not vis.any():
+                    continue                      # out stays 0, lse -inf
+                for h in range(G * d.heads_per_group, (G + 1) * d.heads_per_group):
+                    s = (K[vis] @ q_nope[b, i, h] + KR[vis] @ q_rope[b, i, h]) * d.scale
+                    out[bi, i, h], lse[bi, i, h] = _softmax_attend(s, V[vis])
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
 # Split-KV partials and their log-sum-exp merge (the pages are silent on
 # split-KV; this is the standard exact decomposition of a softmax over a
 # union of disjoint token ranges).

@@ -1,0 +1,132 @@
+"""Pins of the oracle's sparse GQA decode (per-group token selections).
+
+The sparse decode is attention restricted to a listed token subset per KV
+group (GQLA pages: gist.science section 2, subsection "Sparse GQLA";
+pwwt.cn section 5 on the sparse extension).  What fixes the expected values:
+the dense decode when every position is listed, a single listed token
+(softmax over one term is 1), torch's float64 SDPA with a boolean mask over
+the group's whole context, and properties the definition implies (order of
+the list, duplicates, ignored entries, rows that see nothing).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from decode_attention_gqla_amd.inputs import make_case, sparse_indices
+from oracle.gqla_ref import (_expanded_group_views, _expanded_rope_view, decode_gqa_expanded,
+                             decode_gqa_sparse, expand_pages)
+from tests.oracle_util import dims_of, oracle_args
+
+TINY = dict(h_q=4, g=2, r=8, d_R=4, d_nope=4, d_v=6)
+
+
+def setup(ctx, s_q, seed, bs=8):
+    case = make_case(batch=len(ctx), ctx=list(ctx), s_q=s_q, seed=seed, table="random",
+                     dtype=torch.float64, bs=bs, **TINY)
+    d = dims_of(case)
+    q_nope, q_rope, pages, bt, sl, w_uk, w_uv = oracle_args(case)
+    E = expand_pages(pages, w_uk, w_uv, d)
+    return d, q_nope, q_rope, E, bt, sl
+
+
+def rel(a, b):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+def group_rows(E, bt, b, L, d, G):
+    """K, V, rope rows of positions 0..L-1 of sequence b for group G."""
+    K = np.empty((L, d.d_nope)); V = np.empty((L, d.d_v)); R = np.empty((L, d.d_R))
+    for t in range(L):
+        page = E[int(bt[b][t // d.bs])]
+        kv, vv = _expanded_group_views(page, d, G)
+        K[t], V[t], R[t] = kv[t % d.bs], vv[t % d.bs], _expanded_rope_view(page, d)[t % d.bs]
+    return K, V, R
+
+
+@pytest.mark.parametrize("s_q", [1, 2])
+def test_every_position_listed_equals_the_dense_decode(s_q):
+    d, qn, qr, E, bt, sl = setup((9, 30), s_q, seed=201 + s_q)
+    idx = np.full((2, d.g, 30), -1)
+    rng = np.random.default_rng(5)
+    for b in range(2):
+        for G in range(d.g):
+            idx[b, G, : sl[b]] = rng.permutation(int(sl[b]))
+    o_s, l_s = decode_gqa_sparse(qn, qr, E, bt, sl, idx, d)
+    o_d, l_d = decode_gqa_expanded(qn, qr, E, bt, sl, d)
+    assert rel(o_s, o_d) < 1e-12 and np.max(np.abs(l_s - l_d)) < 1e-12
+
+
+def test_single_listed_token_returns_its_value_row():
+    d, qn, qr, E, bt, sl = setup((12, 20), 1, seed=211)
+    idx = np.array([[[3], [11]], [[19], [0]]])
+    out, lse = decode_gqa_sparse(qn, qr, E, bt, sl, idx, d)
+    for b in range(2):
+        for G in range(d.g):
+            t = int(idx[b, G, 0])
+            _, V, _ = group_rows(E, bt, b, int(sl[b]), d, G)
+            for h in range(G * d.heads_per_group, (G + 1) * d.heads_per_group):
+                assert np.array_equal(out[b, 0, h], V[t])
+                assert np.isfinite(lse[b, 0, h])
+
+
+@pytest.mark.parametrize("s_q", [1, 2])
+def test_matches_torch_sdpa_with_a_boolean_mask(s_q):
+    d, qn, qr, E, bt, sl = setup((17, 41), s_q, seed=221 + s_q)
+    idx = sparse_indices(sl.tolist(), d.g, 10, seed=7).numpy()
+    out, lse = decode_gqa_sparse(qn, qr, E, bt, sl, idx, d)
+    for b in range(2):
+        L = int(sl[b])
+        for G in range(d.g):
+            K, V, R = group_rows(E, bt, b, L, d, G)
+            keys = torch.from_numpy(np.concatenate([K, R], axis=1))
+            listed = np.zeros(L, dtype=bool)
+            listed[[t for t in idx[b, G] if 0 <= t < L]] = True
+            for h in range(G * d.heads_per_group, (G + 1) * d.heads_per_group):
+                q = torch.from_numpy(np.concatenate([qn[b, :, h], qr[b, :, h]], axis=1))
+                mask = torch.from_numpy(np.stack([listed & (np.arange(L) <= L - s_q + i)
+                                                  for i in range(s_q)]))
+                ref = torch.nn.functional.scaled_dot_product_attention(
+                    q[None, None], keys[None, None], torch.from_numpy(V)[None, None],
+                    attn_mask=mask[None, None], scale=d.scale)[0, 0].numpy()
+                for i in range(s_q):
+                    if mask[i].any():
+                        assert rel(out[b, i, h], ref[i]) < 1e-12
+                    else:
+                        assert not out[b, i, h].any() and lse[b, i, h] == -math.inf
+
+
+def test_list_order_padding_and_duplicates():
+    d, qn, qr, E, bt, sl = setup((25, 33), 2, seed=231)
+    idx = sparse_indices(sl.tolist(), d.g, 12, seed=9).numpy()
+    o, l = decode_gqa_sparse(qn, qr, E, bt, sl, idx, d)
+    # order of the list is irrelevant
+    o_p, l_p = decode_gqa_sparse(qn, qr, E, bt, sl, idx[:, :, ::-1], d)
+    assert rel(o_p, o) < 1e-12 and np.max(np.abs(l_p - l)) < 1e-12
+    # -1 and positions >= L are ignored
+    pad = np.concatenate([idx, np.full_like(idx, -1), idx * 0 + np.asarray(sl)[:, None, None] + 3],
+                         axis=2)
+    o_x, l_x = decode_gqa_sparse(qn, qr, E, bt, sl, pad, d)
+    assert rel(o_x, o) < 1e-12 and np.max(np.abs(l_x - l)) < 1e-12
+    # every entry listed twice: same weights, the sum of exponentials doubles
+    o_2, l_2 = decode_gqa_sparse(qn, qr, E, bt, sl, np.concatenate([idx, idx], axis=2), d)
+    assert rel(o_2, o) < 1e-12
+    fin = np.isfinite(l)
+    assert np.max(np.abs(l_2[fin] - l[fin] - math.log(2.0))) < 1e-12
+
+
+def test_row_that_sees_no_listed_token_is_empty():
+    # s_q = 2: position L-1 is the second new token; query row 0 cannot see it
+    d, qn, qr, E, bt, sl = setup((10, 16), 2, seed=241)
+    idx = np.stack([np.full((d.g, 1), int(L) - 1) for L in sl])
+    out, lse = decode_gqa_sparse(qn, qr, E, bt, sl, idx, d)
+    assert not out[:, 0].any() and np.all(lse[:, 0] == -math.inf)
+    for b in range(2):
+        for G in range(d.g):
+            _, V, _ = group_rows(E, bt, b, int(sl[b]), d, G)
+            h = G * d.heads_per_group
+            assert np.array_equal(out[b, 1, h], V[int(sl[b]) - 1])
