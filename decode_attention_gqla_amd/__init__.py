@@ -17,7 +17,8 @@ import torch
 
 __all__ = [
     "GqlaError", "Dims", "lib", "gqla_expand_cache", "gqla_decode_mqa_absorb", "gqla_decode_gqa",
-    "gqla_splitkv_combine", "gqla_status_string", "make_split_plan", "latent_page_elems",
+    "gqla_splitkv_combine", "gqla_decode_gqa_sparse", "gqla_sparse_workspace_bytes",
+    "sparse_workspace", "gqla_status_string", "make_split_plan", "latent_page_elems",
     "expanded_page_elems", "decode_mqa_absorb", "decode_gqa", "expand_cache",
     "gqla_mqa_absorb_workspace_bytes", "gqla_mqa_absorb_workspace_offsets", "absorb_workspace",
 ]
@@ -97,6 +98,11 @@ _SIGS = {
                          _f32p, _f32p, _f32p, _vp], ctypes.c_int),
     "gqla_splitkv_combine": ([ctypes.POINTER(Dims), ctypes.c_int32, _i32p, ctypes.c_int32,
                               _f32p, _f32p, _vp, _f32p, _vp], ctypes.c_int),
+    "gqla_decode_gqa_sparse": ([ctypes.POINTER(Dims), ctypes.c_int32, _vp, _vp, _vp, ctypes.c_int64,
+                                _i32p, ctypes.c_int32, _i32p, _i32p, ctypes.c_int32, _vp, _f32p,
+                                _vp, ctypes.c_uint64, _vp], ctypes.c_int),
+    "gqla_sparse_workspace_bytes": ([ctypes.POINTER(Dims), ctypes.c_int32, ctypes.c_int32],
+                                    ctypes.c_uint64),
     "gqla_append_tokens": ([ctypes.POINTER(Dims), ctypes.c_int32, ctypes.c_int32, _vp, _vp,
                             ctypes.c_int64, _i32p, ctypes.c_int32, _i32p, _vp, _vp, _vp, _vp],
                            ctypes.c_int),
@@ -249,6 +255,35 @@ def gqla_decode_gqa(d: Dims, q_nope, q_rope, expanded_pages, block_table, cache_
         a["seqlens"], a["split_offsets"], int(split_tokens), int(total_splits), a["out"],
         a["lse"], a["part_out"], a["part_lse"], _stream(stream))
     _check(st, "gqla_decode_gqa")
+
+
+def gqla_sparse_workspace_bytes(d: Dims, batch: int, topk: int) -> int:
+    return int(lib().gqla_sparse_workspace_bytes(ctypes.byref(d), int(batch), int(topk)))
+
+
+def sparse_workspace(d: Dims, batch: int, topk: int, device="cuda"):
+    """A workspace tensor of the size gqla_decode_gqa_sparse needs."""
+    return torch.empty(max(gqla_sparse_workspace_bytes(d, batch, topk), 16), dtype=torch.uint8,
+                       device=device)
+
+
+def gqla_decode_gqa_sparse(d: Dims, q_nope, q_rope, expanded_pages, block_table, cache_seqlens,
+                           indices, out, lse=None, workspace=None, stream=None) -> None:
+    """Sparse GQA decode: group G of sequence b attends to the positions indices[b, G, :]."""
+    B, mb, a = _decode_common(d, q_nope, q_rope, block_table, cache_seqlens, None, 0, out, lse,
+                              None, None)
+    if indices.dim() != 3 or indices.shape[0] != B or indices.shape[1] != d.num_groups:
+        raise ValueError("indices must be int32 [batch, num_groups, topk]")
+    topk = int(indices.shape[2])
+    if workspace is None:
+        raise ValueError("workspace is required (see gqla_sparse_workspace_bytes)")
+    st = lib().gqla_decode_gqa_sparse(
+        ctypes.byref(d), B, a["q_nope"], a["q_rope"],
+        _ptr(expanded_pages, torch.bfloat16, "expanded_pages"), int(expanded_pages.shape[0]),
+        a["block_table"], mb, a["seqlens"], _ptr(indices, torch.int32, "indices"), topk,
+        a["out"], a["lse"], _ptr(workspace, torch.uint8, "workspace"), int(workspace.numel()),
+        _stream(stream))
+    _check(st, "gqla_decode_gqa_sparse")
 
 
 def gqla_splitkv_combine(d: Dims, split_offsets, part_out, part_lse, out, lse=None,

@@ -78,7 +78,52 @@ __device__ __forceinline__ int vswz(int t) {
   return 2 * (((t & 3) >> LRP) | (((t >> 3) & 1) << (2 - LRP)));
 }
 
-template <int HPG, int SQ, int DN, int DV, int DR>
+// Row code of one entry of a sparse selection (built by sparse_codes_kernel):
+// bits 0..27 the cache row page * 64 + slot of the listed token, bits 28..30
+// the first query row index that may see it (0 .. s_q - 1), or 7 for an entry
+// no row sees (outside [0, L), or padding), whose row is then 0.
+constexpr uint32_t kRowMask = (1u << 28) - 1;
+constexpr uint32_t kInvalidEntry = 7u << 28;
+
+// The 32 row codes of tile `it` of a sparse unit, read through the scalar
+// path (constant address space, wave-uniform address): the vector-memory
+// counter stays reserved for the tile copies.
+struct TileCodes {
+  uint32_t v[32];
+};
+// Lane e (< 32) of the result holds v[e]; lanes 32..63 hold 0.  One
+// v_writelane_b32 per entry (a register-only VALU op with an immediate lane
+// select; this compiler has no builtin for it).
+__device__ __forceinline__ uint32_t spread_codes(const TileCodes& t) {
+  uint32_t r = 0;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(r) : "s"(t.v[e]), "i"(e));
+  return r;
+}
+__device__ __forceinline__ TileCodes load_codes(const uint32_t* unit_codes, int it) {
+  const __attribute__((address_space(4))) uint32_t* cs =
+      (const __attribute__((address_space(4))) uint32_t*)(unit_codes + 32 * it);
+  TileCodes t;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) t.v[e] = cs[e];
+  return t;
+}
+
+// Direct HBM -> LDS copy of 16 bytes per lane from a per-lane 64-bit address
+// (the gather form of dma16; same waiting rules).
+__device__ __forceinline__ void dma16_gather(const void* addr, lds_u8_t* lds_base) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(addr), "s"(m0v) : "memory", "m0");
+}
+
+// SPARSE = false: dense decode of a sequence or split.  SPARSE = true: the
+// unit is (sequence, group) and its tiles are 32 consecutive entries of the
+// group's row codes (sparse GQLA: gist.science section 2, subsection "Sparse
+// GQLA"; every query row of the group shares the selection, so the group's
+// rows stay one dense MFMA tile).  Entries are gathered row by row into the
+// same LDS tile layout, so the tile step is the same apart from its masks.
+template <int HPG, int SQ, int DN, int DV, int DR, bool SPARSE>
 __global__ __launch_bounds__(256) void gqa_decode_kernel(DecodeParams p) {
   using C = GqaCfg<HPG, SQ, DN, DV, DR>;
   constexpr int BS = C::BS, NW = C::NW, KSN = C::KSN, KSR = C::KSR, MT = C::MT;
@@ -100,7 +145,11 @@ __global__ __launch_bounds__(256) void gqa_decode_kernel(DecodeParams p) {
   int b, lo, hi;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);   // this wave's 16-row tile
-  if (p.split_offsets) {
+  if constexpr (SPARSE) {
+    b = u;
+    lo = 0;
+    hi = p.seqlens[b] > 0 ? p.topk_pad : 0;       // no entry is visible in an empty sequence
+  } else if (p.split_offsets) {
     b = split_owner(p.split_offsets, p.batch, u);
     const int j = u - p.split_offsets[b];
     lo = j * p.split_tokens;
@@ -115,43 +164,109 @@ __global__ __launch_bounds__(256) void gqa_decode_kernel(DecodeParams p) {
   const size_t page_elems = (size_t)BS * (g * (DN + DV) + DR);
   const int n_tiles = hi > lo ? (hi - lo + C::TILE - 1) / C::TILE : 0;
   const int32_t* bt = p.block_table + (size_t)b * p.max_blocks;     // wave-uniform
+  const uint32_t* unit_codes = SPARSE ? p.codes + ((size_t)b * g + G) * p.topk_pad : nullptr;
+  uint32_t edge_bits = 0;                         // sparse: tiles in the ring that need masks
+  uint32_t code_ring[C::NBUF];                    // sparse: lane e < 32 holds entry e's code, per buffer
+#pragma unroll
+  for (int r = 0; r < C::NBUF; ++r) code_ring[r] = 0;
 
   // ---- DMA of tile `it` into `dst` (the buffer of tile it % NBUF) ----
-  auto issue_tile = [&](int it) {
+  auto issue_tile = [&](int it, const TileCodes& tc) {
     lds_u8_t* dst = lds + (it % C::NBUF) * C::TILE_BYTES;
-    const int t0 = lo + C::TILE * it;
-    const uint16_t* page = p.cache + (size_t)sload_i32(bt + t0 / BS) * page_elems;
-    const int slot0 = t0 % BS;
-    const uint16_t* kblk = page + (size_t)G * BS * (DN + DV) + slot0 * DN;
-    const uint16_t* vblk = page + (size_t)G * BS * (DN + DV) + BS * DN + slot0 * DV;
-    const uint16_t* rope = page + (size_t)g * BS * (DN + DV) + slot0 * DR;
-    // copy instruction j of the tile (K, then V, then rope) is issued by
-    // wave j % NW
+    if constexpr (SPARSE) {
+      // lanes 0..31 hold the cache rows of the tile's entries; each copy lane
+      // fetches the row of its entry with a cross-lane read
+      const uint32_t cv = spread_codes(tc);
+      const uint32_t rows = cv & kRowMask;
+      uint32_t any = 0;
 #pragma unroll
-    for (int i = 0; i < C::NI_K; ++i) {        // K rows: token-major, chunk swizzled
-      if (i % NW != w) continue;
-      const int P = i * 64 + lane, t = P / KCH, pos = P % KCH;
-      const int ch = pos ^ (kswz(t) & (KCH - 1));
-      dma16(kblk, (uint32_t)(t * DN + ch * 8) * 2u, dst + i * 1024);
-    }
+      for (int e = 0; e < 32; ++e) any |= tc.v[e];
+      const int slot = it % C::NBUF;
 #pragma unroll
-    for (int i = 0; i < C::NI_V; ++i) {        // V rows: token-major, chunk swizzled
-      if ((C::NI_K + i) % NW != w) continue;
-      const int P = i * 64 + lane, t = P / VCH, pos = P % VCH;
-      const int ch = pos ^ vswz<DV>(t);
-      dma16(vblk, (uint32_t)(t * DV + ch * 8) * 2u, dst + C::K_BYTES + i * 1024);
-    }
+      for (int r = 0; r < C::NBUF; ++r) code_ring[r] = r == slot ? cv : code_ring[r];
+      const int bit = 1 << slot;
+      edge_bits = (any >> 28) ? (edge_bits | bit) : (edge_bits & ~bit);
+      // Wave w issues copies w, w + NW, ... of the tile (the same ones as in
+      // the dense case); each region (K, V, rope) holds a multiple of NW
+      // copies, so copy k of this wave lies in a region known at compile
+      // time.  First every copy lane's entry row (cross-lane reads, one wait),
+      // then the copies.
+      static_assert(C::NI_K % NW == 0 && C::NI_V % NW == 0 && C::NI_R % NW == 0, "copies per region");
+      constexpr int KW = C::NI_K / NW, VW = C::NI_V / NW;
+      auto entry_of = [&](int k) {                // tile entry copied by this lane in copy k, and its chunk
+        int P, chunks;
+        if (k < KW) {
+          P = (k * NW + w) * 64 + lane;
+          chunks = KCH;
+        } else if (k < KW + VW) {
+          P = ((k - KW) * NW + w) * 64 + lane;
+          chunks = VCH;
+        } else {
+          P = min(((k - KW - VW) * NW + w) * 64 + lane, C::TILE * RCH - 1);   // partial last copy: duplicate
+          chunks = RCH;
+        }
+        return int2{P / chunks, P % chunks};
+      };
+      uint32_t r[C::NIW];
 #pragma unroll
-    for (int i = 0; i < C::NI_R; ++i) {        // rope rows: token-major, chunk swizzled
-      if ((C::NI_K + C::NI_V + i) % NW != w) continue;
-      int P = i * 64 + lane;
-      if (P >= C::TILE * RCH) P = C::TILE * RCH - 1;   // partial last instruction: duplicate
-      const int t = P / RCH, pos = P % RCH;
-      const int ch = pos ^ (rswz(t) & (RCH - 1));
-      dma16(rope, (uint32_t)(t * DR + ch * 8) * 2u, dst + C::K_BYTES + C::V_BYTES + i * 1024);
+      for (int k = 0; k < C::NIW; ++k) r[k] = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * entry_of(k).x, (int)rows);
+#pragma unroll
+      for (int k = 0; k < C::NIW; ++k) {
+        const int2 tp = entry_of(k);
+        const int t = tp.x, pos = tp.y;
+        const uint16_t* page = p.cache + (size_t)(r[k] >> 6) * page_elems;
+        const int slot = (int)(r[k] & 63u);
+        if (k < KW) {                              // K rows: token-major, chunk swizzled
+          const int ch = pos ^ (kswz(t) & (KCH - 1));
+          dma16_gather(page + (size_t)G * BS * (DN + DV) + slot * DN + ch * 8, dst + (k * NW + w) * 1024);
+        } else if (k < KW + VW) {                  // V rows
+          const int ch = pos ^ vswz<DV>(t);
+          dma16_gather(page + (size_t)G * BS * (DN + DV) + BS * DN + slot * DV + ch * 8,
+                       dst + C::K_BYTES + ((k - KW) * NW + w) * 1024);
+        } else {                                   // rope rows
+          const int ch = pos ^ (rswz(t) & (RCH - 1));
+          dma16_gather(page + (size_t)g * BS * (DN + DV) + slot * DR + ch * 8,
+                       dst + C::K_BYTES + C::V_BYTES + ((k - KW - VW) * NW + w) * 1024);
+        }
+      }
+    } else {
+      const int t0 = lo + C::TILE * it;
+      const uint16_t* page = p.cache + (size_t)sload_i32(bt + t0 / BS) * page_elems;
+      const int slot0 = t0 % BS;
+      const uint16_t* kblk = page + (size_t)G * BS * (DN + DV) + slot0 * DN;
+      const uint16_t* vblk = page + (size_t)G * BS * (DN + DV) + BS * DN + slot0 * DV;
+      const uint16_t* rope = page + (size_t)g * BS * (DN + DV) + slot0 * DR;
+      // copy instruction j of the tile (K, then V, then rope) is issued by
+      // wave j % NW
+#pragma unroll
+      for (int i = 0; i < C::NI_K; ++i) {        // K rows: token-major, chunk swizzled
+        if (i % NW != w) continue;
+        const int P = i * 64 + lane, t = P / KCH, pos = P % KCH;
+        const int ch = pos ^ (kswz(t) & (KCH - 1));
+        dma16(kblk, (uint32_t)(t * DN + ch * 8) * 2u, dst + i * 1024);
+      }
+#pragma unroll
+      for (int i = 0; i < C::NI_V; ++i) {        // V rows: token-major, chunk swizzled
+        if ((C::NI_K + i) % NW != w) continue;
+        const int P = i * 64 + lane, t = P / VCH, pos = P % VCH;
+        const int ch = pos ^ vswz<DV>(t);
+        dma16(vblk, (uint32_t)(t * DV + ch * 8) * 2u, dst + C::K_BYTES + i * 1024);
+      }
+#pragma unroll
+      for (int i = 0; i < C::NI_R; ++i) {        // rope rows: token-major, chunk swizzled
+        if ((C::NI_K + C::NI_V + i) % NW != w) continue;
+        int P = i * 64 + lane;
+        if (P >= C::TILE * RCH) P = C::TILE * RCH - 1;   // partial last instruction: duplicate
+        const int t = P / RCH, pos = P % RCH;
+        const int ch = pos ^ (rswz(t) & (RCH - 1));
+        dma16(rope, (uint32_t)(t * DR + ch * 8) * 2u, dst + C::K_BYTES + C::V_BYTES + i * 1024);
+      }
     }
   };
-
+  auto codes_of = [&](int it) {
+    if constexpr (SPARSE) return load_codes(unit_codes, it);
+    else return TileCodes{};
+  };
   // Query rows of this wave's tile as B operands (Q^T): lane (q, c) holds 8
   // dims of row 16 w + c.
   const int rho = 16 * w + c;
@@ -173,19 +288,30 @@ __global__ __launch_bounds__(256) void gqa_decode_kernel(DecodeParams p) {
   // The query loads complete before the first tile copy is issued, so the
   // compiler's own wait tracking has nothing pending inside the tile loop.
   vm_wait<0>();
-  for (int i = 0; i < C::LA && i < n_tiles; ++i) issue_tile(i);
+  for (int i = 0; i < C::LA && i < n_tiles; ++i) issue_tile(i, codes_of(i));
 
   f32x4 o[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
   const int nvis = L - SQ + (rvalid ? rho % SQ : SQ - 1) + 1;   // tokens t < nvis are visible
+  const int iq_row = rvalid ? rho % SQ : SQ - 1;  // this lane's query row index
 
   // One tile: S^T, the online softmax, O^T += V^T P^T.  EDGE: the tile
   // reaches the causal bound or the sequence end, so logits are masked and
   // the V rows of tokens past the end (which may hold anything) are zeroed.
   auto tile_step = [&](const lds_u8_t* buf, int t0, auto edge) {
     constexpr bool EDGE = decltype(edge)::value;
+    // sparse edge tiles: the codes of this lane's 8 entries 8q .. 8q+7
+    uint32_t ecode[8];
+    if constexpr (SPARSE && EDGE) {
+      const int slot = ((t0 - lo) / C::TILE) % C::NBUF;
+      uint32_t cv = 0;
+#pragma unroll
+      for (int r = 0; r < C::NBUF; ++r) cv = r == slot ? code_ring[r] : cv;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ecode[j] = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (8 * q + j), (int)cv);
+    }
     f32x4 s[2];
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
@@ -217,7 +343,8 @@ __global__ __launch_bounds__(256) void gqa_decode_kernel(DecodeParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float v = s[st][i] * p.scale_log2;
-        if constexpr (EDGE) v = (t0 + 8 * q + 4 * st + i < nvis) ? v : -INFINITY;
+        if constexpr (EDGE && SPARSE) v = ((int)(ecode[4 * st + i] >> 28) <= iq_row) ? v : -INFINITY;
+        else if constexpr (EDGE) v = (t0 + 8 * q + 4 * st + i < nvis) ? v : -INFINITY;
         x[4 * st + i] = v;
         mx = fmaxf(mx, v);
       }
@@ -243,7 +370,15 @@ __global__ __launch_bounds__(256) void gqa_decode_kernel(DecodeParams p) {
       u32x4 pk = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
       pb = __builtin_bit_cast(bf16x8, pk);
     }
-    const int keep = EDGE ? min(max(L - (t0 + 8 * q), 0), 8) : 8;
+    const int keep = (EDGE && !SPARSE) ? min(max(L - (t0 + 8 * q), 0), 8) : 8;
+    // sparse: V elements of entries no row sees are zeroed (their rows may hold anything)
+    u32x4 vkeep = {~0u, ~0u, ~0u, ~0u};
+    if constexpr (EDGE && SPARSE) {
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2)
+        vkeep[w2] = (ecode[2 * w2] >= kInvalidEntry ? 0u : 0x0000ffffu) |
+                    (ecode[2 * w2 + 1] >= kInvalidEntry ? 0u : 0xffff0000u);
+    }
     // transposing reads: source lane (q, c) of read h addresses dims
     // 16 mt + 4 (c & 3) .. +3 of token 8 q + 4 h + c / 4, so lane (q, c)
     // receives dim 16 mt + c of tokens 8 q + 4 h .. +3
@@ -257,12 +392,16 @@ __global__ __launch_bounds__(256) void gqa_decode_kernel(DecodeParams p) {
       s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vr0 + (lch ^ sw0) * 16));
       s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vr1 + (lch ^ sw1) * 16));
       bf16x8 v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      if constexpr (EDGE) v = keep_first(v, keep);
+      if constexpr (EDGE && SPARSE) v = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, v) & vkeep);
+      else if constexpr (EDGE) v = keep_first(v, keep);
       o[mt] = mfma16(v, pb, o[mt]);
     }
   };
 
   for (int it = 0; it < n_tiles; ++it) {
+    // sparse: the row codes of tile it + LA, read before the wait so their
+    // latency overlaps it (clamped to a real tile; unused past the end)
+    const TileCodes nxt = codes_of(min(it + C::LA, n_tiles - 1));
     // this wave's copies of tile it landed (those of the next LA-1 tiles may
     // be in flight); after the barrier every wave's copies of tile it landed
     // and every wave is done with tile it-1, whose buffer takes tile it+LA
@@ -271,12 +410,14 @@ __global__ __launch_bounds__(256) void gqa_decode_kernel(DecodeParams p) {
     else if (ahead == 1) vm_wait<C::NIW>();
     else vm_wait<0>();
     if constexpr (NW > 1) __syncthreads();
-    if (it + C::LA < n_tiles) issue_tile(it + C::LA);
+    if (it + C::LA < n_tiles) issue_tile(it + C::LA, nxt);
     const lds_u8_t* buf = lds + (it % C::NBUF) * C::TILE_BYTES;
     const int t0 = lo + C::TILE * it;
     // only tiles that reach the first causal bound (L - s_q + 1), the last
-    // one or two of the sequence, mask logits and V rows
-    if (t0 + C::TILE > L - SQ + 1) tile_step(buf, t0, std::true_type{});
+    // one or two of the sequence, mask logits and V rows; sparse tiles do
+    // when an entry is invalid or visible to later query rows only
+    const bool edge = SPARSE ? ((edge_bits >> (it % C::NBUF)) & 1) != 0 : (t0 + C::TILE > L - SQ + 1);
+    if (edge) tile_step(buf, t0, std::true_type{});
     else tile_step(buf, t0, std::false_type{});
   }
 
@@ -308,21 +449,24 @@ __global__ __launch_bounds__(256) void gqa_decode_kernel(DecodeParams p) {
 }
 
 // Host-side launcher: returns hipError_t of the launch.
-template <int HPG, int SQ, int DN, int DV, int DR>
+template <int HPG, int SQ, int DN, int DV, int DR, bool SPARSE>
 hipError_t launch_gqa(const DecodeParams& p, hipStream_t stream) {
   const int g = p.num_groups;
   const int rounds = (p.num_units + 7) / 8;
   const unsigned grid = (unsigned)rounds * 8u * (unsigned)g;
-  hipLaunchKernelGGL((gqa_decode_kernel<HPG, SQ, DN, DV, DR>), dim3(grid), dim3(64 * GqaCfg<HPG, SQ, DN, DV, DR>::NW), 0,
-                     stream, p);
+  hipLaunchKernelGGL((gqa_decode_kernel<HPG, SQ, DN, DV, DR, SPARSE>), dim3(grid),
+                     dim3(64 * GqaCfg<HPG, SQ, DN, DV, DR>::NW), 0, stream, p);
   return hipGetLastError();
 }
 
 hipError_t gqa_dispatch(int hpg, int sq, int dn, int dv, int dr, const DecodeParams& p,
                         hipStream_t stream, bool* supported) {
   *supported = true;
-#define GQLA_GQA_CASE(HPG, SQ, DN, DV, DR) \
-  if (hpg == HPG && sq == SQ && dn == DN && dv == DV && dr == DR) return launch_gqa<HPG, SQ, DN, DV, DR>(p, stream);
+  const bool sparse = p.codes != nullptr;
+#define GQLA_GQA_CASE(HPG, SQ, DN, DV, DR)                                            \
+  if (hpg == HPG && sq == SQ && dn == DN && dv == DV && dr == DR)                     \
+    return sparse ? launch_gqa<HPG, SQ, DN, DV, DR, true>(p, stream)                  \
+                  : launch_gqa<HPG, SQ, DN, DV, DR, false>(p, stream);
   GQLA_GQA_CASE(16, 1, 128, 128, 64)
   GQLA_GQA_CASE(16, 2, 128, 128, 64)
   GQLA_GQA_CASE(32, 1, 128, 128, 64)
@@ -334,6 +478,35 @@ hipError_t gqa_dispatch(int hpg, int sq, int dn, int dv, int dr, const DecodePar
 #undef GQLA_GQA_CASE
   *supported = false;
   return hipSuccess;
+}
+
+// Row codes of a sparse selection: one thread per (sequence, group, entry)
+// of the padded lists (the format is described with kRowMask above).
+__global__ __launch_bounds__(256) void sparse_codes_kernel(SparseCodeParams p) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per_seq = (int64_t)p.num_groups * p.topk_pad;
+  if (i >= (int64_t)p.batch * per_seq) return;
+  const int b = (int)(i / per_seq);
+  const int G = (int)((i % per_seq) / p.topk_pad);
+  const int e = (int)(i % p.topk_pad);
+  uint32_t code = kInvalidEntry;
+  if (e < p.topk) {
+    const int t = p.indices[((int64_t)b * p.num_groups + G) * p.topk + e];
+    const int L = p.seqlens[b];
+    if (t >= 0 && t < L && t / p.block_size < p.max_blocks) {
+      const int32_t page = p.block_table[(int64_t)b * p.max_blocks + t / p.block_size];
+      if (page >= 0 && page < p.num_pages)
+        code = ((uint32_t)page * (uint32_t)p.block_size + (uint32_t)(t % p.block_size)) |
+               ((uint32_t)max(t - (L - p.s_q), 0) << 28);
+    }
+  }
+  p.codes[i] = code;
+}
+
+hipError_t sparse_codes_launch(const SparseCodeParams& p, hipStream_t stream) {
+  const int64_t n = (int64_t)p.batch * p.num_groups * p.topk_pad;
+  hipLaunchKernelGGL(sparse_codes_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p);
+  return hipGetLastError();
 }
 
 }  // namespace gqla

@@ -17,6 +17,7 @@ hipError_t expand_dispatch(int r, int dn, int dv, int dr, const ExpandParams& p,
                            bool* supported);
 hipError_t combine_dispatch(int dv, const CombineParams& p, hipStream_t stream, bool* supported);
 hipError_t append_launch(const AppendParams& p, int r, int dn, int dv, int dr, hipStream_t stream, bool* supported);
+hipError_t sparse_codes_launch(const SparseCodeParams& p, hipStream_t stream);
 }  // namespace gqla
 
 namespace {
@@ -112,6 +113,8 @@ gqla::DecodeParams make_params(const gqla_dims* d, int32_t batch, const void* q_
   p.wuvT = nullptr;
   p.olat = nullptr;
   p.olse = nullptr;
+  p.codes = nullptr;
+  p.topk_pad = 0;
   return p;
 }
 
@@ -313,6 +316,52 @@ int gqla_decode_gqa(const gqla_dims* d, int32_t batch, const void* q_nope, const
   st = finish(e, ok);
   if (st != GQLA_OK || !split_offsets || !out) return st;
   return enqueue_combine(d, batch, split_offsets, part_out, part_lse, out, lse, (hipStream_t)stream);
+}
+
+uint64_t gqla_sparse_workspace_bytes(const gqla_dims* d, int32_t batch, int32_t topk) {
+  if (!d || d->num_groups <= 0 || batch <= 0 || topk <= 0 || topk > INT32_MAX - 31) return 0;
+  const uint64_t pad = ((uint64_t)topk + 31) / 32 * 32;
+  return (uint64_t)batch * (uint64_t)d->num_groups * pad * 4u;
+}
+
+int gqla_decode_gqa_sparse(const gqla_dims* d, int32_t batch, const void* q_nope, const void* q_rope,
+                           const void* expanded_pages, int64_t num_pages, const int32_t* block_table,
+                           int32_t max_blocks, const int32_t* cache_seqlens, const int32_t* indices,
+                           int32_t topk, void* out, float* lse, void* workspace,
+                           uint64_t workspace_bytes, void* stream) {
+  int st = check_decode(d, batch, q_nope, q_rope, expanded_pages, block_table, max_blocks,
+                        cache_seqlens, nullptr, 0, 0, out, lse, nullptr, nullptr, true);
+  if (st != GQLA_OK) return st;
+  if (!indices || topk <= 0 || topk > INT32_MAX - 31 || num_pages <= 0) return GQLA_ERR_INVALID_ARG;
+  if (num_pages > ((int64_t)1 << 28) / d->block_size) return GQLA_ERR_INVALID_ARG;   // 28-bit row codes
+  if (!aligned4(indices)) return GQLA_ERR_MISALIGNED;
+  if (batch == 0) return GQLA_OK;
+  if (!workspace || workspace_bytes < gqla_sparse_workspace_bytes(d, batch, topk)) return GQLA_ERR_INVALID_ARG;
+  if (!aligned16(workspace)) return GQLA_ERR_MISALIGNED;
+  const int32_t topk_pad = (topk + 31) / 32 * 32;
+  gqla::SparseCodeParams cp;
+  cp.indices = indices;
+  cp.block_table = block_table;
+  cp.seqlens = cache_seqlens;
+  cp.codes = (uint32_t*)workspace;
+  cp.num_pages = num_pages;
+  cp.batch = batch;
+  cp.num_groups = d->num_groups;
+  cp.topk = topk;
+  cp.topk_pad = topk_pad;
+  cp.max_blocks = max_blocks;
+  cp.block_size = d->block_size;
+  cp.s_q = d->s_q;
+  if (gqla::sparse_codes_launch(cp, (hipStream_t)stream) != hipSuccess) return GQLA_ERR_HIP;
+  gqla::DecodeParams p = make_params(d, batch, q_nope, q_rope, expanded_pages, block_table,
+                                     max_blocks, cache_seqlens, nullptr, nullptr, nullptr, 0, 0, out,
+                                     lse, nullptr, nullptr);
+  p.codes = (const uint32_t*)workspace;
+  p.topk_pad = topk_pad;
+  bool ok = true;
+  hipError_t e = gqla::gqa_dispatch(d->num_heads / d->num_groups, d->s_q, d->d_nope, d->d_v,
+                                    d->d_rope, p, (hipStream_t)stream, &ok);
+  return finish(e, ok);
 }
 
 int gqla_splitkv_combine(const gqla_dims* d, int32_t batch, const int32_t* split_offsets,

@@ -27,6 +27,23 @@ struct DecodeParams {
   int32_t split_tokens;          // tokens per split (split launch)
   int32_t num_units;             // total splits, or batch when unsplit
   float scale_log2;              // softmax scale * log2(e)
+  const uint32_t* codes;         // sparse GQA: row codes [B][g][topk_pad], else nullptr
+  int32_t topk_pad;              // sparse GQA: entries per (sequence, group), a multiple of 32
+};
+
+struct SparseCodeParams {
+  const int32_t* indices;        // [B][g][topk] token positions
+  const int32_t* block_table;    // [B][max_blocks]
+  const int32_t* seqlens;        // [B]
+  uint32_t* codes;               // [B][g][topk_pad]
+  int64_t num_pages;
+  int32_t batch;
+  int32_t num_groups;
+  int32_t topk;
+  int32_t topk_pad;
+  int32_t max_blocks;
+  int32_t block_size;
+  int32_t s_q;
 };
 
 struct ExpandParams {

@@ -204,6 +204,40 @@ int gqla_decode_gqa(const gqla_dims* d, int32_t batch, const void* q_nope, const
                     int32_t split_tokens, int32_t total_splits, void* out, float* lse,
                     float* part_out, float* part_lse, void* stream);
 
+/* Sparse GQA decode over per-group token selections (sparse GQLA:
+ * gist.science section 2, subsection "Sparse GQLA"; pwwt.cn section 5 on the
+ * sparse extension; ai-feeds.com "Methods", the optional sparse extension).
+ * Each KV group attends to its own listed subset of the cached tokens, shared
+ * by all h_q/g heads and all s_q query rows of the group, so the group's rows
+ * stay one dense matrix tile.  How the subset is chosen (an indexer) is left
+ * to the caller.  Arguments as for gqla_decode_gqa without a split plan, and:
+ *   num_pages  pages in expanded_pages (>= 1, at most 2^28 / block_size);
+ *   indices    int32 [batch][g][topk]: token positions of sequence b chosen
+ *              for group G.  Entries outside [0, cache_seqlens[b]), or whose
+ *              block-table page is outside [0, num_pages), are ignored (-1
+ *              pads a short list); an entry listed twice counts twice; query
+ *              row i still sees only positions <= L_b - s_q + i.  A row that
+ *              sees no entry gets out = 0 and lse = -inf.
+ *   topk       entries per list (>= 1).
+ *   out, lse   as for gqla_decode_gqa (out required).
+ *   workspace  device scratch of at least gqla_sparse_workspace_bytes(d,
+ *              batch, topk) bytes, 16-byte aligned, owned by the caller and
+ *              not shared by calls that may run concurrently.  It receives
+ *              each entry's resolved cache row, uint32 [batch][g][topk
+ *              rounded up to 32]: bits 0..27 page * block_size + slot, bits
+ *              28..30 the first query row that sees the entry (7: none).
+ * Two kernels are enqueued on `stream`: the row resolution, then the decode. */
+int gqla_decode_gqa_sparse(const gqla_dims* d, int32_t batch, const void* q_nope,
+                           const void* q_rope, const void* expanded_pages, int64_t num_pages,
+                           const int32_t* block_table, int32_t max_blocks,
+                           const int32_t* cache_seqlens, const int32_t* indices, int32_t topk,
+                           void* out, float* lse, void* workspace, uint64_t workspace_bytes,
+                           void* stream);
+
+/* Bytes of workspace gqla_decode_gqa_sparse needs; 0 for d == NULL,
+ * batch <= 0 or topk <= 0. */
+uint64_t gqla_sparse_workspace_bytes(const gqla_dims* d, int32_t batch, int32_t topk);
+
 /* Log-sum-exp merge of split partials (the pages are silent on split-KV; this
  * is the exact decomposition of a softmax over disjoint token ranges):
  *   m = max_s lse_s, w_s = exp(lse_s - m), out = sum_s w_s o_s / sum_s w_s

@@ -166,6 +166,38 @@ def test_append_argument_errors(lib):
               None, None, None, None) == UNSUPPORTED
 
 
+def test_sparse_argument_errors(lib):
+    d = Dims.make(128, 8, 512, 64, 128, 128, 2)
+    fn = lib.gqla_decode_gqa_sparse
+    need = 2 * 8 * 64 * 4                  # batch 2, 8 groups, 40 entries padded to 64, 4 bytes
+    assert lib.gqla_sparse_workspace_bytes(ctypes.byref(d), 2, 40) == need
+    assert lib.gqla_sparse_workspace_bytes(ctypes.byref(d), 0, 40) == 0
+    assert lib.gqla_sparse_workspace_bytes(ctypes.byref(d), 2, 0) == 0
+    assert lib.gqla_sparse_workspace_bytes(None, 2, 40) == 0
+
+    def call(dd=d, batch=2, qn=A, pages=A, num_pages=8, idx=A, topk=40, out=A, ws=A, ws_bytes=need):
+        # d, batch, q_nope, q_rope, expanded, num_pages, table, max_blocks, lens, indices, topk,
+        # out, lse, workspace, workspace_bytes, stream
+        return fn(dd, batch, qn, A, pages, num_pages, A, 4, A, idx, topk, out, None, ws, ws_bytes,
+                  None)
+    # every call below fails its argument checks on the host, before any launch
+    assert call(topk=0) == INVALID
+    assert call(idx=None) == INVALID
+    assert call(num_pages=0) == INVALID
+    assert call(num_pages=(1 << 28) // 64 + 1) == INVALID        # rows must fit 28 bits
+    assert call(ws=None) == INVALID
+    assert call(ws_bytes=need - 1) == INVALID
+    assert call(out=None) == INVALID
+    assert call(qn=None) == INVALID
+    assert call(dd=None) == INVALID
+    assert call(idx=ODD) == MISALIGNED
+    assert call(ws=ODD) == MISALIGNED
+    assert call(pages=ODD) == MISALIGNED
+    assert call(dd=ctypes.byref(Dims.make(96, 8, 512, 64, 128, 128, 2))) == UNSUPPORTED
+    assert call(batch=-1) == INVALID
+    assert call(batch=0) == OK                                   # nothing to do, nothing enqueued
+
+
 def test_binding_rejects_cpu_tensors_and_wrong_dtypes(lib):
     d = Dims.make(16, 2, 64, 16, 32, 32, 1)
     q = torch.zeros(1, 1, 16, 32, dtype=torch.bfloat16)
