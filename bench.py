@@ -202,6 +202,45 @@ def measure_g4(G, rf, config_case, steps: int, absorb_split: int):
             "gqa_split_tokens": gsplit, "paths": res}
 
 
+def measure_sparse(G, rf, d2, qn, qr, E, bt, sl, lens, steps: int, topks=(2048, 512)):
+    """Sparse GQLA on the GQA path: each of the 8 groups of every sequence attends to its own
+    seeded random selection of `topk` distinct positions (stand-in for an indexer's top-k),
+    over the same expanded cache and s_q = 2 queries as the dense GQA path.  One call = the
+    row-resolution kernel + the gathering decode."""
+    import torch
+    from decode_attention_gqla_amd.inputs import sparse_indices
+    B = len(lens)
+    res = {}
+    for topk in topks:
+        idx_h = sparse_indices(lens, d2.num_groups, topk, seed=topk)
+        idx = idx_h.to("cuda")
+        ws = G.sparse_workspace(d2, B, topk)
+        out = torch.empty(B, 2, 128, 128, dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty(B, 2, 128, dtype=torch.float32, device="cuda")
+
+        def fn():
+            G.gqla_decode_gqa_sparse(d2, qn, qr, E, bt, sl, idx, out, lse=lse, workspace=ws)
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        evs = []
+        for _ in range(steps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+        med = us[len(us) // 2]
+        w = rf.work_gqa_sparse(idx_h.numpy(), lens, 128, 8, 64, 128, 128, 2)
+        res[f"topk_{topk}"] = {"us_median": med, "tok_s": B * 2 / (med * 1e-6), "alg_bytes": w.bytes,
+                               "bound": w.bound(), "achieved_GBps": w.bytes / (med * 1e-6) / 1e9,
+                               "roofline_us": w.roofline_us(), "roofline_frac": w.roofline_us() / med}
+    return {"workload": "sparse GQA, DeepSeek-V3 shape, batch 64, context 4096, s_q = 2, topk distinct "
+                        "random positions per (sequence, group)", "calls": res}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -348,8 +387,9 @@ def main():
                     "tok_s_absorb": ea.tokens_per_s, "tok_s_gqa": eg.tokens_per_s}
     variants = None
     if not args.only and not args.no_variants:
-        log("(g, s_q) = (4, 1) variant")
+        log("variants: append, sparse GQA, (g, s_q) = (4, 1)")
         variants = {"append_2_tokens": measure_append(G, d2, pages, bt, sl, lens, w_uk, w_uv, E, args.steps),
+                    "sparse_gqa": measure_sparse(G, rf, d2, qg_n, qg_r, E, bt, sl, lens, args.steps),
                     "g4_sq1": measure_g4(G, rf, config_case, args.steps, args.absorb_split)}
     cpu = None
     if not args.no_cpu and not args.only:

@@ -115,6 +115,30 @@ def work_gqa(seqlens, h_q, g, d_R, d_nope, d_v, s_q) -> Work:
     return Work(bytes=cache + q + out, flops=attn, cache_bytes=cache)
 
 
+def work_gqa_sparse(indices, seqlens, h_q, g, d_R, d_nope, d_v, s_q) -> Work:
+    """Algorithmic work of one gqla_decode_gqa_sparse call: every valid entry of group G moves
+    its K, V and rope rows once (each group gathers its own rows, rope included), plus the
+    queries, the index lists and the output; FLOPs count each (row, visible entry) pair."""
+    B = len(seqlens)
+    hpg = h_q // g
+    entries = 0
+    pairs = 0
+    n_idx = 0
+    for b in range(B):
+        L = int(seqlens[b])
+        for G in range(g):
+            ts = [int(t) for t in indices[b][G]]
+            n_idx += len(ts)
+            valid = [t for t in ts if 0 <= t < L]
+            entries += len(valid)
+            pairs += sum(1 for i in range(s_q) for t in valid if t <= L - s_q + i)
+    cache = entries * (d_nope + d_v + d_R) * BF16
+    q = B * s_q * h_q * (d_nope + d_R) * BF16
+    out = B * s_q * h_q * d_v * BF16
+    return Work(bytes=cache + q + out + n_idx * 4, flops=pairs * hpg * 2 * (d_nope + d_R + d_v),
+                cache_bytes=cache)
+
+
 def work_expand(num_pages, bs, g, r, d_R, d_nope, d_v) -> Work:
     tokens = num_pages * bs
     read = tokens * (r + d_R) * BF16 + g * r * (d_nope + d_v) * BF16

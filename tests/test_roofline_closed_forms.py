@@ -73,3 +73,27 @@ def test_per_launch_work_matches_hand_count_for_the_dsv3_batch():
     # two MTP rows see 4095 and 4096 tokens
     assert g.flops == 64 * (4095 + 4096) * 128 * 2 * 320
     assert g.bound() == "hbm" and w.bound() == "hbm"
+
+
+def test_sparse_work_with_every_position_listed_relates_to_the_dense_count():
+    # every position listed once: the same (row, token) pairs as the dense decode, and the
+    # rope row read once per group instead of once per token
+    lens = [100, 37]
+    idx = [[list(range(L)) + [-1, L + 3] for _ in range(8)] for L in lens]
+    sp = rf.work_gqa_sparse(idx, lens, 128, 8, 64, 128, 128, 2)
+    de = rf.work_gqa(lens, 128, 8, 64, 128, 128, 2)
+    assert sp.flops == de.flops
+    assert sp.cache_bytes == de.cache_bytes + sum(lens) * 7 * 64 * 2
+    # queries and output as for the dense call, plus 4 bytes per listed index
+    assert sp.bytes - sp.cache_bytes == de.bytes - de.cache_bytes + sum(8 * (L + 2) * 4 for L in lens)
+
+
+def test_sparse_work_hand_count_for_the_bench_configuration():
+    # batch 64, 8 groups, 2048 distinct entries per group, all older than the new tokens
+    lens = [4096] * 64
+    idx = [[list(range(0, 4096, 2))] * 8] * 64
+    w = rf.work_gqa_sparse(idx, lens, 128, 8, 64, 128, 128, 2)
+    assert w.cache_bytes == 64 * 8 * 2048 * 640
+    assert w.bytes == 64 * 8 * 2048 * 640 + 64 * 2 * 128 * 192 * 2 + 64 * 2 * 128 * 128 * 2 \
+        + 64 * 8 * 2048 * 4
+    assert w.flops == 64 * 8 * 2048 * 2 * 16 * 2 * 320
