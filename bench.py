@@ -241,6 +241,57 @@ def measure_sparse(G, rf, d2, qn, qr, E, bt, sl, lens, steps: int, topks=(2048, 
                         "random positions per (sequence, group)", "calls": res}
 
 
+def measure_sparse_ragged(G, rf, config_case, steps: int, topk: int = 2048, splits=(0, 512, 1024)):
+    """Sparse GQA at small batch: the ragged long-context mix (16 sequences, contexts log-uniform
+    in [1024, 32768]) with s_q = 2 and `topk` random positions per (sequence, group); one
+    workgroup per (sequence, group) is only 128 workgroups, so the call is also measured split into
+    ranges of entries merged by log-sum-exp."""
+    import torch
+    from decode_attention_gqla_amd.inputs import sparse_indices
+    case = config_case("dsv3_ragged", 2)
+    d = G.Dims.of(case)
+    dev = "cuda"
+    pages, bt, sl = case.pages.to(dev), case.block_table.to(dev), case.seqlens.to(dev)
+    w_uk, w_uv = case.w_uk.to(dev), case.w_uv.to(dev)
+    qn, qr = case.q_nope.to(dev), case.q_rope.to(dev)
+    lens = [int(x) for x in case.seqlens]
+    B = len(lens)
+    E = G.expand_cache(d, pages, w_uk, w_uv)
+    del pages
+    idx_h = sparse_indices(lens, d.num_groups, topk, seed=topk + 1)
+    idx = idx_h.to(dev)
+    w = rf.work_gqa_sparse(idx_h.numpy(), lens, 128, 8, 64, 128, 128, 2)
+    out = torch.empty(B, 2, 128, 128, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(B, 2, 128, dtype=torch.float32, device=dev)
+    res = {}
+    for split in splits:
+        ws = G.sparse_workspace(d, B, topk, split)
+
+        def fn():
+            G.gqla_decode_gqa_sparse(d, qn, qr, E, bt, sl, idx, out, lse=lse, workspace=ws,
+                                     split_entries=split)
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        evs = []
+        for _ in range(steps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+        med = us[len(us) // 2]
+        res[f"split_{split}" if split else "unsplit"] = {
+            "us_median": med, "tok_s": B * 2 / (med * 1e-6), "achieved_GBps": w.bytes / (med * 1e-6) / 1e9,
+            "roofline_us": w.roofline_us(), "roofline_frac": w.roofline_us() / med}
+    del E
+    return {"workload": f"sparse GQA, ragged long-context mix: 16 sequences, contexts log-uniform in "
+                        f"[1024, 32768], s_q = 2, {topk} random positions per (sequence, group)",
+            "alg_bytes": w.bytes, "calls": res}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -390,6 +441,7 @@ def main():
         log("variants: append, sparse GQA, (g, s_q) = (4, 1)")
         variants = {"append_2_tokens": measure_append(G, d2, pages, bt, sl, lens, w_uk, w_uv, E, args.steps),
                     "sparse_gqa": measure_sparse(G, rf, d2, qg_n, qg_r, E, bt, sl, lens, args.steps),
+                    "sparse_gqa_ragged": measure_sparse_ragged(G, rf, config_case, args.steps),
                     "g4_sq1": measure_g4(G, rf, config_case, args.steps, args.absorb_split)}
     cpu = None
     if not args.no_cpu and not args.only:

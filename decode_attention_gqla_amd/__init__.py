@@ -18,7 +18,7 @@ import torch
 __all__ = [
     "GqlaError", "Dims", "lib", "gqla_expand_cache", "gqla_decode_mqa_absorb", "gqla_decode_gqa",
     "gqla_splitkv_combine", "gqla_decode_gqa_sparse", "gqla_sparse_workspace_bytes",
-    "sparse_workspace", "gqla_status_string", "make_split_plan", "latent_page_elems",
+    "sparse_workspace", "gqla_sparse_workspace_offsets", "gqla_status_string", "make_split_plan", "latent_page_elems",
     "expanded_page_elems", "decode_mqa_absorb", "decode_gqa", "expand_cache",
     "gqla_mqa_absorb_workspace_bytes", "gqla_mqa_absorb_workspace_offsets", "absorb_workspace",
 ]
@@ -99,10 +99,12 @@ _SIGS = {
     "gqla_splitkv_combine": ([ctypes.POINTER(Dims), ctypes.c_int32, _i32p, ctypes.c_int32,
                               _f32p, _f32p, _vp, _f32p, _vp], ctypes.c_int),
     "gqla_decode_gqa_sparse": ([ctypes.POINTER(Dims), ctypes.c_int32, _vp, _vp, _vp, ctypes.c_int64,
-                                _i32p, ctypes.c_int32, _i32p, _i32p, ctypes.c_int32, _vp, _f32p,
-                                _vp, ctypes.c_uint64, _vp], ctypes.c_int),
-    "gqla_sparse_workspace_bytes": ([ctypes.POINTER(Dims), ctypes.c_int32, ctypes.c_int32],
-                                    ctypes.c_uint64),
+                                _i32p, ctypes.c_int32, _i32p, _i32p, ctypes.c_int32, ctypes.c_int32,
+                                _vp, _f32p, _vp, ctypes.c_uint64, _vp], ctypes.c_int),
+    "gqla_sparse_workspace_bytes": ([ctypes.POINTER(Dims), ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_int32], ctypes.c_uint64),
+    "gqla_sparse_workspace_offsets": ([ctypes.POINTER(Dims), ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_int32, ctypes.POINTER(ctypes.c_uint64)], ctypes.c_int),
     "gqla_append_tokens": ([ctypes.POINTER(Dims), ctypes.c_int32, ctypes.c_int32, _vp, _vp,
                             ctypes.c_int64, _i32p, ctypes.c_int32, _i32p, _vp, _vp, _vp, _vp],
                            ctypes.c_int),
@@ -257,19 +259,32 @@ def gqla_decode_gqa(d: Dims, q_nope, q_rope, expanded_pages, block_table, cache_
     _check(st, "gqla_decode_gqa")
 
 
-def gqla_sparse_workspace_bytes(d: Dims, batch: int, topk: int) -> int:
-    return int(lib().gqla_sparse_workspace_bytes(ctypes.byref(d), int(batch), int(topk)))
+def gqla_sparse_workspace_bytes(d: Dims, batch: int, topk: int, split_entries: int = 0) -> int:
+    return int(lib().gqla_sparse_workspace_bytes(ctypes.byref(d), int(batch), int(topk),
+                                                 int(split_entries)))
 
 
-def sparse_workspace(d: Dims, batch: int, topk: int, device="cuda"):
+def gqla_sparse_workspace_offsets(d: Dims, batch: int, topk: int, split_entries: int = 0) -> list[int]:
+    """Byte offsets of the sparse workspace regions: row codes, split plan, partials, partial
+    lse, end."""
+    off = (ctypes.c_uint64 * 5)()
+    _check(lib().gqla_sparse_workspace_offsets(ctypes.byref(d), int(batch), int(topk),
+                                               int(split_entries), off),
+           "gqla_sparse_workspace_offsets")
+    return [int(x) for x in off]
+
+
+def sparse_workspace(d: Dims, batch: int, topk: int, split_entries: int = 0, device="cuda"):
     """A workspace tensor of the size gqla_decode_gqa_sparse needs."""
-    return torch.empty(max(gqla_sparse_workspace_bytes(d, batch, topk), 16), dtype=torch.uint8,
-                       device=device)
+    return torch.empty(max(gqla_sparse_workspace_bytes(d, batch, topk, split_entries), 16),
+                       dtype=torch.uint8, device=device)
 
 
 def gqla_decode_gqa_sparse(d: Dims, q_nope, q_rope, expanded_pages, block_table, cache_seqlens,
-                           indices, out, lse=None, workspace=None, stream=None) -> None:
-    """Sparse GQA decode: group G of sequence b attends to the positions indices[b, G, :]."""
+                           indices, out, lse=None, workspace=None, split_entries=0,
+                           stream=None) -> None:
+    """Sparse GQA decode: group G of sequence b attends to the positions indices[b, G, :]
+    (optionally split into ranges of ``split_entries`` entries, merged by log-sum-exp)."""
     B, mb, a = _decode_common(d, q_nope, q_rope, block_table, cache_seqlens, None, 0, out, lse,
                               None, None)
     if indices.dim() != 3 or indices.shape[0] != B or indices.shape[1] != d.num_groups:
@@ -281,8 +296,8 @@ def gqla_decode_gqa_sparse(d: Dims, q_nope, q_rope, expanded_pages, block_table,
         ctypes.byref(d), B, a["q_nope"], a["q_rope"],
         _ptr(expanded_pages, torch.bfloat16, "expanded_pages"), int(expanded_pages.shape[0]),
         a["block_table"], mb, a["seqlens"], _ptr(indices, torch.int32, "indices"), topk,
-        a["out"], a["lse"], _ptr(workspace, torch.uint8, "workspace"), int(workspace.numel()),
-        _stream(stream))
+        int(split_entries), a["out"], a["lse"], _ptr(workspace, torch.uint8, "workspace"),
+        int(workspace.numel()), _stream(stream))
     _check(st, "gqla_decode_gqa_sparse")
 
 

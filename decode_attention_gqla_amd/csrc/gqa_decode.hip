@@ -20,6 +20,7 @@
 // read from the token-major V rows with ds_read_b64_tr_b16.  The LDS copies
 // are XOR-swizzled in 16-byte chunks so every operand read is bank-conflict
 // free.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hip.h"
@@ -145,10 +146,17 @@ __global__ __launch_bounds__(256) void gqa_decode_kernel(DecodeParams p) {
   int b, lo, hi;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);   // this wave's 16-row tile
-  if constexpr (SPARSE) {
-    b = u;
-    lo = 0;
-    hi = p.seqlens[b] > 0 ? p.topk_pad : 0;       // no entry is visible in an empty sequence
+  if constexpr (SPARSE) {                         // units: (sequence, entry range) x group
+    if (p.split_offsets) {
+      b = split_owner(p.split_offsets, p.batch, u);
+      lo = (u - p.split_offsets[b]) * p.split_tokens;
+      hi = min(lo + p.split_tokens, p.topk_pad);
+    } else {
+      b = u;
+      lo = 0;
+      hi = p.topk_pad;
+    }
+    if (p.seqlens[b] <= 0) hi = lo;               // no entry is visible in an empty sequence
   } else if (p.split_offsets) {
     b = split_owner(p.split_offsets, p.batch, u);
     const int j = u - p.split_offsets[b];
@@ -164,7 +172,7 @@ __global__ __launch_bounds__(256) void gqa_decode_kernel(DecodeParams p) {
   const size_t page_elems = (size_t)BS * (g * (DN + DV) + DR);
   const int n_tiles = hi > lo ? (hi - lo + C::TILE - 1) / C::TILE : 0;
   const int32_t* bt = p.block_table + (size_t)b * p.max_blocks;     // wave-uniform
-  const uint32_t* unit_codes = SPARSE ? p.codes + ((size_t)b * g + G) * p.topk_pad : nullptr;
+  const uint32_t* unit_codes = SPARSE ? p.codes + ((size_t)b * g + G) * p.topk_pad + lo : nullptr;
   uint32_t edge_bits = 0;                         // sparse: tiles in the ring that need masks
   uint32_t code_ring[C::NBUF];                    // sparse: lane e < 32 holds entry e's code, per buffer
 #pragma unroll
@@ -485,6 +493,7 @@ hipError_t gqa_dispatch(int hpg, int sq, int dn, int dv, int dr, const DecodePar
 __global__ __launch_bounds__(256) void sparse_codes_kernel(SparseCodeParams p) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t per_seq = (int64_t)p.num_groups * p.topk_pad;
+  if (p.split_offsets && i <= p.batch) p.split_offsets[i] = (int32_t)(i * p.splits_per_seq);
   if (i >= (int64_t)p.batch * per_seq) return;
   const int b = (int)(i / per_seq);
   const int G = (int)((i % per_seq) / p.topk_pad);
@@ -504,7 +513,7 @@ __global__ __launch_bounds__(256) void sparse_codes_kernel(SparseCodeParams p) {
 }
 
 hipError_t sparse_codes_launch(const SparseCodeParams& p, hipStream_t stream) {
-  const int64_t n = (int64_t)p.batch * p.num_groups * p.topk_pad;
+  const int64_t n = std::max<int64_t>((int64_t)p.batch * p.num_groups * p.topk_pad, (int64_t)p.batch + 1);
   hipLaunchKernelGGL(sparse_codes_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }

@@ -318,27 +318,61 @@ int gqla_decode_gqa(const gqla_dims* d, int32_t batch, const void* q_nope, const
   return enqueue_combine(d, batch, split_offsets, part_out, part_lse, out, lse, (hipStream_t)stream);
 }
 
-uint64_t gqla_sparse_workspace_bytes(const gqla_dims* d, int32_t batch, int32_t topk) {
-  if (!d || d->num_groups <= 0 || batch <= 0 || topk <= 0 || topk > INT32_MAX - 31) return 0;
+int gqla_sparse_workspace_offsets(const gqla_dims* d, int32_t batch, int32_t topk,
+                                  int32_t split_entries, uint64_t* offsets) {
+  if (!d || !offsets || d->num_groups <= 0 || d->num_heads <= 0 || d->s_q <= 0 || d->d_v <= 0 ||
+      batch <= 0 || topk <= 0 || topk > INT32_MAX - 31 || split_entries < 0)
+    return GQLA_ERR_INVALID_ARG;
   const uint64_t pad = ((uint64_t)topk + 31) / 32 * 32;
-  return (uint64_t)batch * (uint64_t)d->num_groups * pad * 4u;
+  auto up = [](uint64_t x) { return (x + 255) / 256 * 256; };
+  const uint64_t codes = (uint64_t)batch * (uint64_t)d->num_groups * pad * 4u;
+  uint64_t o = up(codes);
+  offsets[0] = 0;
+  if (split_entries == 0) {
+    offsets[1] = offsets[2] = offsets[3] = offsets[4] = codes;
+    return GQLA_OK;
+  }
+  const uint64_t units = (uint64_t)batch * ((pad + (uint64_t)split_entries - 1) / (uint64_t)split_entries);
+  const uint64_t rows = units * (uint64_t)d->s_q * (uint64_t)d->num_heads;
+  offsets[1] = o;                                   // split plan, int32 [batch + 1]
+  o = up(o + ((uint64_t)batch + 1) * 4u);
+  offsets[2] = o;                                   // partial outputs, fp32 [units][s_q][h_q][d_v]
+  o = up(o + rows * (uint64_t)d->d_v * 4u);
+  offsets[3] = o;                                   // partial lse, fp32 [units][s_q][h_q]
+  offsets[4] = o + rows * 4u;                       // end
+  return GQLA_OK;
+}
+
+uint64_t gqla_sparse_workspace_bytes(const gqla_dims* d, int32_t batch, int32_t topk, int32_t split_entries) {
+  uint64_t off[5];
+  if (gqla_sparse_workspace_offsets(d, batch, topk, split_entries, off) != GQLA_OK) return 0;
+  return off[4];
 }
 
 int gqla_decode_gqa_sparse(const gqla_dims* d, int32_t batch, const void* q_nope, const void* q_rope,
                            const void* expanded_pages, int64_t num_pages, const int32_t* block_table,
                            int32_t max_blocks, const int32_t* cache_seqlens, const int32_t* indices,
-                           int32_t topk, void* out, float* lse, void* workspace,
-                           uint64_t workspace_bytes, void* stream) {
+                           int32_t topk, int32_t split_entries, void* out, float* lse,
+                           void* workspace, uint64_t workspace_bytes, void* stream) {
   int st = check_decode(d, batch, q_nope, q_rope, expanded_pages, block_table, max_blocks,
                         cache_seqlens, nullptr, 0, 0, out, lse, nullptr, nullptr, true);
   if (st != GQLA_OK) return st;
   if (!indices || topk <= 0 || topk > INT32_MAX - 31 || num_pages <= 0) return GQLA_ERR_INVALID_ARG;
   if (num_pages > ((int64_t)1 << 28) / d->block_size) return GQLA_ERR_INVALID_ARG;   // 28-bit row codes
+  if (split_entries < 0 || split_entries % 32 != 0) return GQLA_ERR_BAD_SPLIT_PLAN;
   if (!aligned4(indices)) return GQLA_ERR_MISALIGNED;
   if (batch == 0) return GQLA_OK;
-  if (!workspace || workspace_bytes < gqla_sparse_workspace_bytes(d, batch, topk)) return GQLA_ERR_INVALID_ARG;
+  uint64_t off[5];
+  if (gqla_sparse_workspace_offsets(d, batch, topk, split_entries, off) != GQLA_OK) return GQLA_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < off[4]) return GQLA_ERR_INVALID_ARG;
   if (!aligned16(workspace)) return GQLA_ERR_MISALIGNED;
   const int32_t topk_pad = (topk + 31) / 32 * 32;
+  const int32_t n_split = split_entries ? (topk_pad + split_entries - 1) / split_entries : 0;
+  if (split_entries && (int64_t)batch * n_split > INT32_MAX) return GQLA_ERR_BAD_SPLIT_PLAN;
+  unsigned char* ws = (unsigned char*)workspace;
+  int32_t* plan = split_entries ? (int32_t*)(ws + off[1]) : nullptr;
+  float* part_out = split_entries ? (float*)(ws + off[2]) : nullptr;
+  float* part_lse = split_entries ? (float*)(ws + off[3]) : nullptr;
   gqla::SparseCodeParams cp;
   cp.indices = indices;
   cp.block_table = block_table;
@@ -352,16 +386,20 @@ int gqla_decode_gqa_sparse(const gqla_dims* d, int32_t batch, const void* q_nope
   cp.max_blocks = max_blocks;
   cp.block_size = d->block_size;
   cp.s_q = d->s_q;
+  cp.split_offsets = plan;
+  cp.splits_per_seq = n_split;
   if (gqla::sparse_codes_launch(cp, (hipStream_t)stream) != hipSuccess) return GQLA_ERR_HIP;
   gqla::DecodeParams p = make_params(d, batch, q_nope, q_rope, expanded_pages, block_table,
-                                     max_blocks, cache_seqlens, nullptr, nullptr, nullptr, 0, 0, out,
-                                     lse, nullptr, nullptr);
+                                     max_blocks, cache_seqlens, nullptr, nullptr, plan, split_entries,
+                                     batch * n_split, out, lse, part_out, part_lse);
   p.codes = (const uint32_t*)workspace;
   p.topk_pad = topk_pad;
   bool ok = true;
   hipError_t e = gqla::gqa_dispatch(d->num_heads / d->num_groups, d->s_q, d->d_nope, d->d_v,
                                     d->d_rope, p, (hipStream_t)stream, &ok);
-  return finish(e, ok);
+  st = finish(e, ok);
+  if (st != GQLA_OK || !split_entries) return st;
+  return enqueue_combine(d, batch, plan, part_out, part_lse, out, lse, (hipStream_t)stream);
 }
 
 int gqla_splitkv_combine(const gqla_dims* d, int32_t batch, const int32_t* split_offsets,

@@ -44,6 +44,8 @@ struct SparseCodeParams {
   int32_t max_blocks;
   int32_t block_size;
   int32_t s_q;
+  int32_t* split_offsets;        // [B + 1] split plan (i * splits_per_seq), or nullptr
+  int32_t splits_per_seq;
 };
 
 struct ExpandParams {

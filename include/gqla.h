@@ -219,24 +219,46 @@ int gqla_decode_gqa(const gqla_dims* d, int32_t batch, const void* q_nope, const
  *              row i still sees only positions <= L_b - s_q + i.  A row that
  *              sees no entry gets out = 0 and lse = -inf.
  *   topk       entries per list (>= 1).
+ *   split_entries  0: one workgroup per (sequence, group) over its whole
+ *              list; else a multiple of 32: each list (rounded up to 32
+ *              entries) is cut into ranges of this many entries, one
+ *              workgroup per (sequence, range, group), whose fp32 partials
+ *              are merged by log-sum-exp as gqla_splitkv_combine merges them
+ *              (a third kernel).  Splitting fills the GPU at small batch.
  *   out, lse   as for gqla_decode_gqa (out required).
  *   workspace  device scratch of at least gqla_sparse_workspace_bytes(d,
- *              batch, topk) bytes, 16-byte aligned, owned by the caller and
- *              not shared by calls that may run concurrently.  It receives
- *              each entry's resolved cache row, uint32 [batch][g][topk
- *              rounded up to 32]: bits 0..27 page * block_size + slot, bits
- *              28..30 the first query row that sees the entry (7: none).
- * Two kernels are enqueued on `stream`: the row resolution, then the decode. */
+ *              batch, topk, split_entries) bytes, 16-byte aligned, owned by
+ *              the caller and not shared by calls that may run concurrently.
+ *              Regions (byte offsets from gqla_sparse_workspace_offsets):
+ *                [0] each entry's resolved cache row, uint32 [batch][g][topk
+ *                    rounded up to 32]: bits 0..27 page * block_size + slot,
+ *                    bits 28..30 the first query row that sees the entry (7:
+ *                    none);
+ *                [1] with a split: the split plan, int32 [batch + 1]
+ *                    (b * ranges per list);
+ *                [2], [3] with a split: the partial outputs fp32 [batch *
+ *                    ranges][s_q][h_q][d_v] and their lse fp32 [batch *
+ *                    ranges][s_q][h_q];
+ *                [4] the end.
+ * Kernels are enqueued on `stream`: the row resolution, the decode, and with a
+ * split the merge. */
 int gqla_decode_gqa_sparse(const gqla_dims* d, int32_t batch, const void* q_nope,
                            const void* q_rope, const void* expanded_pages, int64_t num_pages,
                            const int32_t* block_table, int32_t max_blocks,
                            const int32_t* cache_seqlens, const int32_t* indices, int32_t topk,
-                           void* out, float* lse, void* workspace, uint64_t workspace_bytes,
-                           void* stream);
+                           int32_t split_entries, void* out, float* lse, void* workspace,
+                           uint64_t workspace_bytes, void* stream);
 
-/* Bytes of workspace gqla_decode_gqa_sparse needs; 0 for d == NULL,
- * batch <= 0 or topk <= 0. */
-uint64_t gqla_sparse_workspace_bytes(const gqla_dims* d, int32_t batch, int32_t topk);
+/* Bytes of workspace gqla_decode_gqa_sparse needs; 0 for the arguments
+ * gqla_sparse_workspace_offsets rejects. */
+uint64_t gqla_sparse_workspace_bytes(const gqla_dims* d, int32_t batch, int32_t topk,
+                                     int32_t split_entries);
+
+/* Byte offsets of the sparse workspace regions listed above (offsets[0..4]);
+ * GQLA_ERR_INVALID_ARG for d == NULL, offsets == NULL, batch <= 0, topk <= 0
+ * or split_entries < 0. */
+int gqla_sparse_workspace_offsets(const gqla_dims* d, int32_t batch, int32_t topk,
+                                  int32_t split_entries, uint64_t* offsets);
 
 /* Log-sum-exp merge of split partials (the pages are silent on split-KV; this
  * is the exact decomposition of a softmax over disjoint token ranges):

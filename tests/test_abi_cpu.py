@@ -170,16 +170,25 @@ def test_sparse_argument_errors(lib):
     d = Dims.make(128, 8, 512, 64, 128, 128, 2)
     fn = lib.gqla_decode_gqa_sparse
     need = 2 * 8 * 64 * 4                  # batch 2, 8 groups, 40 entries padded to 64, 4 bytes
-    assert lib.gqla_sparse_workspace_bytes(ctypes.byref(d), 2, 40) == need
-    assert lib.gqla_sparse_workspace_bytes(ctypes.byref(d), 0, 40) == 0
-    assert lib.gqla_sparse_workspace_bytes(ctypes.byref(d), 2, 0) == 0
-    assert lib.gqla_sparse_workspace_bytes(None, 2, 40) == 0
+    assert lib.gqla_sparse_workspace_bytes(ctypes.byref(d), 2, 40, 0) == need
+    assert lib.gqla_sparse_workspace_bytes(ctypes.byref(d), 0, 40, 0) == 0
+    assert lib.gqla_sparse_workspace_bytes(ctypes.byref(d), 2, 0, 0) == 0
+    assert lib.gqla_sparse_workspace_bytes(ctypes.byref(d), 2, 40, -32) == 0
+    assert lib.gqla_sparse_workspace_bytes(None, 2, 40, 0) == 0
+    # with a split of 32 entries: 2 ranges per list; plan, partials and their lse follow the codes
+    off = G.gqla_sparse_workspace_offsets(d, 2, 40, 32)
+    units, rows = 2 * 2, 2 * 2 * 2 * 128
+    assert off[0] == 0 and off[1] == need and off[1] % 256 == 0
+    assert off[2] == off[1] + 256 and off[3] == off[2] + rows * 128 * 4
+    assert off[4] == off[3] + rows * 4 and rows == units * 2 * 128
+    assert lib.gqla_sparse_workspace_bytes(ctypes.byref(d), 2, 40, 32) == off[4]
 
-    def call(dd=d, batch=2, qn=A, pages=A, num_pages=8, idx=A, topk=40, out=A, ws=A, ws_bytes=need):
+    def call(dd=d, batch=2, qn=A, pages=A, num_pages=8, idx=A, topk=40, split=0, out=A, ws=A,
+             ws_bytes=need):
         # d, batch, q_nope, q_rope, expanded, num_pages, table, max_blocks, lens, indices, topk,
-        # out, lse, workspace, workspace_bytes, stream
-        return fn(dd, batch, qn, A, pages, num_pages, A, 4, A, idx, topk, out, None, ws, ws_bytes,
-                  None)
+        # split_entries, out, lse, workspace, workspace_bytes, stream
+        return fn(dd, batch, qn, A, pages, num_pages, A, 4, A, idx, topk, split, out, None, ws,
+                  ws_bytes, None)
     # every call below fails its argument checks on the host, before any launch
     assert call(topk=0) == INVALID
     assert call(idx=None) == INVALID
@@ -187,6 +196,9 @@ def test_sparse_argument_errors(lib):
     assert call(num_pages=(1 << 28) // 64 + 1) == INVALID        # rows must fit 28 bits
     assert call(ws=None) == INVALID
     assert call(ws_bytes=need - 1) == INVALID
+    assert call(split=32, ws_bytes=need) == INVALID              # a split needs the larger workspace
+    assert call(split=33) == BADSPLIT
+    assert call(split=-32) == BADSPLIT
     assert call(out=None) == INVALID
     assert call(qn=None) == INVALID
     assert call(dd=None) == INVALID

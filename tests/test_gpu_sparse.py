@@ -20,14 +20,14 @@ from tests.oracle_util import dims_of
 pytestmark = pytest.mark.gpu
 
 
-def run_sparse(gc, E, idx_host):
+def run_sparse(gc, E, idx_host, split=0):
     d, B = gc.d, gc.q_nope.shape[0]
     idx = idx_host.to("cuda")
     out = torch.empty(B, d.s_q, d.num_heads, d.d_v, dtype=torch.bfloat16, device="cuda")
     lse = torch.empty(B, d.s_q, d.num_heads, dtype=torch.float32, device="cuda")
-    ws = G.sparse_workspace(d, B, idx.shape[2])
+    ws = G.sparse_workspace(d, B, idx.shape[2], split)
     G.gqla_decode_gqa_sparse(d, gc.q_nope, gc.q_rope, E, gc.block_table, gc.seqlens, idx, out,
-                             lse=lse, workspace=ws)
+                             lse=lse, workspace=ws, split_entries=split)
     return out, lse
 
 
@@ -158,3 +158,48 @@ def test_sparse_is_deterministic_and_writes_only_its_outputs():
     assert torch.equal(first, out)
     assert torch.all(buf[n_out:] == 3.0) and torch.all(lbuf[n_lse:] == 5.0)
     assert torch.all(wbuf[n_ws:] == 9)
+
+
+SPLIT_CASES = [
+    ("tiny", 2, dict(batch=2, ctx=(256, 70)), 100, 32, 0.1),     # 4 ranges, the last ragged
+    ("dsv3", 2, dict(batch=3, ctx=(4096, 1000, 77)), 2048, 512, 0.05),   # ranges of padding only
+    ("dsv3_g4", 1, dict(batch=2, ctx=(1500, 33)), 300, 64, 0.0),
+]
+
+
+@pytest.mark.parametrize("name,s_q,kw,topk,split,invalid", SPLIT_CASES)
+def test_split_sparse_matches_oracle_and_the_unsplit_call(name, s_q, kw, topk, split, invalid):
+    log(f"sparse/split {name} s_q={s_q} {kw} topk={topk} split={split}")
+    case = config_case(name, s_q, poison=True, table="random", **kw)
+    d = dims_of(case)
+    gc = GpuCase(case)
+    E = gc.expand()
+    idx = sparse_indices(gc.seqlens_host, d.g, topk, seed=401 + topk, invalid_frac=invalid)
+    out, lse = run_sparse(gc, E, idx, split=split)
+    ref_u, _ = run_sparse(gc, E, idx)
+    torch.cuda.synchronize()
+    ex_o, ex_l = decode_gqa_sparse(f64(case.q_nope), f64(case.q_rope), f64(E),
+                                   case.block_table.numpy(), case.seqlens.numpy(), idx.numpy(), d)
+    check(out, lse, ex_o, ex_l, "split out vs oracle over GPU-expanded cache", max_rel=8e-3,
+          rel_l2=4e-3)
+    assert_close(f64(out), f64(ref_u), "split vs unsplit", max_rel=8e-3, rel_l2=4e-3)
+
+
+def test_split_sparse_writes_only_its_workspace():
+    log("sparse/split canary")
+    case = config_case("dsv3", 2, batch=2, ctx=(700, 2000), poison=True)
+    gc = GpuCase(case)
+    E = gc.expand()
+    d, B = gc.d, 2
+    idx = sparse_indices(gc.seqlens_host, d.num_groups, 600, seed=6).to("cuda")
+    n_ws = G.gqla_sparse_workspace_bytes(d, B, 600, 128)
+    off = G.gqla_sparse_workspace_offsets(d, B, 600, 128)
+    assert off[4] == n_ws
+    wbuf = torch.full((n_ws + 4096,), 9, dtype=torch.uint8, device="cuda")
+    out = torch.empty(B, d.s_q, d.num_heads, d.d_v, dtype=torch.bfloat16, device="cuda")
+    G.gqla_decode_gqa_sparse(d, gc.q_nope, gc.q_rope, E, gc.block_table, gc.seqlens, idx, out,
+                             workspace=wbuf[:n_ws], split_entries=128)
+    torch.cuda.synchronize()
+    assert torch.all(wbuf[n_ws:] == 9)
+    plan = wbuf[off[1]: off[1] + 4 * (B + 1)].view(torch.int32).cpu().tolist()
+    assert plan == [0, 5, 10]                                   # 608 padded entries -> 5 ranges
