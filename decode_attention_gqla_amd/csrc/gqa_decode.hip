@@ -10,8 +10,10 @@
 // which stay in registers.  Each 32-token tile of the group's K and V blocks
 // (both token-major) and of the shared rope key is copied HBM -> LDS by direct
 // DMA (global_load_lds_dwordx4, three tiles ahead, no VGPR staging; the waves
-// share the copy instructions and the tile), then read as bf16 MFMA operands
-// (the copies are waited for explicitly with vmcnt, see dma16):
+// share the copy instructions and the tile; K and V, read once, with the
+// non-temporal policy, the rope tile shared by the g group workgroups through
+// L2 without it), then read as bf16 MFMA operands (the copies are waited for
+// explicitly with vmcnt, see dma16):
 //   S^T[token][row] = K[token][:] . Q[row][:]        (A = cache rows, B = Q^T)
 //   O^T[dim][row]  += V^T[dim][token] . P^T[token][row]
 // The token order inside a tile is relabelled so that the S^T accumulator lane
@@ -111,11 +113,17 @@ __device__ __forceinline__ TileCodes load_codes(const uint32_t* unit_codes, int 
 }
 
 // Direct HBM -> LDS copy of 16 bytes per lane from a per-lane 64-bit address
-// (the gather form of dma16; same waiting rules).
+// (the gather form of dma16; same waiting rules); NT: non-temporal policy,
+// as dma16_nt.
+template <bool NT>
 __device__ __forceinline__ void dma16_gather(const void* addr, lds_u8_t* lds_base) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(addr), "s"(m0v) : "memory", "m0");
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+                 :: "v"(addr), "s"(m0v) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(addr), "s"(m0v) : "memory", "m0");
 }
 
 // SPARSE = false: dense decode of a sequence or split.  SPARSE = true: the
@@ -226,15 +234,15 @@ __global__ __launch_bounds__(256) void gqa_decode_kernel(DecodeParams p) {
         const int slot = (int)(r[k] & 63u);
         if (k < KW) {                              // K rows: token-major, chunk swizzled
           const int ch = pos ^ (kswz(t) & (KCH - 1));
-          dma16_gather(page + (size_t)G * BS * (DN + DV) + slot * DN + ch * 8, dst + (k * NW + w) * 1024);
+          dma16_gather<true>(page + (size_t)G * BS * (DN + DV) + slot * DN + ch * 8, dst + (k * NW + w) * 1024);
         } else if (k < KW + VW) {                  // V rows
           const int ch = pos ^ vswz<DV>(t);
-          dma16_gather(page + (size_t)G * BS * (DN + DV) + BS * DN + slot * DV + ch * 8,
-                       dst + C::K_BYTES + ((k - KW) * NW + w) * 1024);
+          dma16_gather<true>(page + (size_t)G * BS * (DN + DV) + BS * DN + slot * DV + ch * 8,
+                             dst + C::K_BYTES + ((k - KW) * NW + w) * 1024);
         } else {                                   // rope rows
           const int ch = pos ^ (rswz(t) & (RCH - 1));
-          dma16_gather(page + (size_t)g * BS * (DN + DV) + slot * DR + ch * 8,
-                       dst + C::K_BYTES + C::V_BYTES + ((k - KW - VW) * NW + w) * 1024);
+          dma16_gather<false>(page + (size_t)g * BS * (DN + DV) + slot * DR + ch * 8,
+                              dst + C::K_BYTES + C::V_BYTES + ((k - KW - VW) * NW + w) * 1024);
         }
       }
     } else {
@@ -251,14 +259,14 @@ __global__ __launch_bounds__(256) void gqa_decode_kernel(DecodeParams p) {
         if (i % NW != w) continue;
         const int P = i * 64 + lane, t = P / KCH, pos = P % KCH;
         const int ch = pos ^ (kswz(t) & (KCH - 1));
-        dma16(kblk, (uint32_t)(t * DN + ch * 8) * 2u, dst + i * 1024);
+        dma16_nt(kblk, (uint32_t)(t * DN + ch * 8) * 2u, dst + i * 1024);
       }
 #pragma unroll
       for (int i = 0; i < C::NI_V; ++i) {        // V rows: token-major, chunk swizzled
         if ((C::NI_K + i) % NW != w) continue;
         const int P = i * 64 + lane, t = P / VCH, pos = P % VCH;
         const int ch = pos ^ vswz<DV>(t);
-        dma16(vblk, (uint32_t)(t * DV + ch * 8) * 2u, dst + C::K_BYTES + i * 1024);
+        dma16_nt(vblk, (uint32_t)(t * DV + ch * 8) * 2u, dst + C::K_BYTES + i * 1024);
       }
 #pragma unroll
       for (int i = 0; i < C::NI_R; ++i) {        // rope rows: token-major, chunk swizzled
