@@ -673,27 +673,37 @@ __global__ __launch_bounds__(512) void absorb_merge_kernel(DecodeParams p) {
 // rows of the batch.  Workgroup = 4 waves x 32 query rows of one group and a
 // chunk of up to 128 latent dims; D = q_abs^T (m = latent, n = row), so each
 // W_UK operand feeds the wave's two 16-row tiles and each lane stores 4
-// consecutive latent values of one row.  Every operand load is issued before
-// the first product, so the wave waits for memory once.
+// consecutive latent values of one row.  The chunk's W_UK rows are one
+// contiguous block: the workgroup stages it in LDS once with 1 KB loads (each
+// wave then reads its operands from there), and the query rows are loaded
+// before the wait, so the workgroup waits for memory once.
 template <int HPG, int SQ, int R, int DR, int DN>
 __device__ __forceinline__ void absorb_q_block(const DecodeParams& p, int bx, int G, int bz) {
   constexpr int ROW = R + DR, KD = DN / 32, MT = R / 16;
   constexpr int MTC = MT < 8 ? MT : 8;               // latent tiles per workgroup (blockIdx.z)
   constexpr int NT = 2;                              // 16-row tiles per wave
+  constexpr int WR = 16 * MTC;                       // W_UK rows staged
+  constexpr int CPR = DN / 8;                        // 16-byte chunks per W_UK row
+  constexpr int NCK = WR * CPR / 256;                // chunks per thread
+  // row stride 2 DN + 32 bytes: the operand read of lane (q, c) starts at bank
+  // 4 ((DN / 8 + 2) c + q) mod 64, which keeps every 16-lane pass of a 16-byte
+  // read on 64 distinct banks
+  constexpr int WSTR = 2 * DN + 32;
+  static_assert(WR * CPR % 256 == 0, "staging tiling");
+  __shared__ __attribute__((aligned(16))) unsigned char wl_raw[WR * WSTR];
+  lds_u8_t* const wl = (lds_u8_t*)wl_raw;
   const int g = p.num_groups, H = HPG * g;
   const int rows_g = p.batch * SQ * HPG;             // query rows of one group
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c = lane & 15, q = lane >> 4;
   const int r0 = (bx * 4 + w) * 16 * NT;             // first group-row of this wave
-  if (r0 >= rows_g) return;
-  // group-row gr = (b * SQ + i) * HPG + hl  ->  head h = G*HPG + hl
-  const uint16_t* W = p.w_uk + (size_t)G * R * DN;
   const int mt0 = bz * MTC;
-  bf16x8 wa[MTC][KD];
+  const uint16_t* W = p.w_uk + ((size_t)G * R + 16 * mt0) * DN;
+  u32x4 wv[NCK];
 #pragma unroll
-  for (int m = 0; m < MTC; ++m)
-#pragma unroll
-    for (int kd = 0; kd < KD; ++kd) wa[m][kd] = ld_bf16x8(W + (size_t)(16 * (mt0 + m) + c) * DN + 32 * kd + 8 * q);
+  for (int i = 0; i < NCK; ++i) wv[i] = *reinterpret_cast<const u32x4*>(W + 8 * (tid + 256 * i));
+  // group-row gr = (b * SQ + i) * HPG + hl  ->  head h = G*HPG + hl; rows past
+  // the batch load row 0 and are not stored
   bf16x8 qn[NT][KD];
   size_t qrow[NT];
   bool valid[NT];
@@ -701,22 +711,35 @@ __device__ __forceinline__ void absorb_q_block(const DecodeParams& p, int bx, in
   for (int nt = 0; nt < NT; ++nt) {
     const int gr = r0 + 16 * nt + c;
     valid[nt] = gr < rows_g;
-    const int hl = gr % HPG, bi = gr / HPG;          // bi = b * SQ + i
+    const int gc = valid[nt] ? gr : 0;
+    const int hl = gc % HPG, bi = gc / HPG;          // bi = b * SQ + i
     qrow[nt] = (size_t)bi * H + G * HPG + hl;
 #pragma unroll
-    for (int kd = 0; kd < KD; ++kd)
-      qn[nt][kd] = valid[nt] ? ld_bf16x8(p.q_nope + qrow[nt] * DN + 32 * kd + 8 * q) : zero_bf16x8();
+    for (int kd = 0; kd < KD; ++kd) qn[nt][kd] = ld_bf16x8(p.q_nope + qrow[nt] * DN + 32 * kd + 8 * q);
   }
 #pragma unroll
+  for (int i = 0; i < NCK; ++i) {
+    const int e = tid + 256 * i;
+    *(lds_u32x4_t*)(wl + (e / CPR) * WSTR + 16 * (e % CPR)) = wv[i];
+  }
+  __syncthreads();
+  if (r0 >= rows_g) return;
+#pragma unroll
   for (int m = 0; m < MTC; ++m) {
+    f32x4 acc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kd = 0; kd < KD; ++kd) {
+      const bf16x8 a = __builtin_bit_cast(bf16x8, *(const lds_u32x4_t*)(wl + (16 * m + c) * WSTR + 64 * kd + 16 * q));
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma16(a, qn[nt][kd], acc[nt]);
+    }
+    // lane (q, c): latent 16 (mt0 + m) + 4q .. +3 of row (nt, c)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kd = 0; kd < KD; ++kd) acc = mfma16(wa[m][kd], qn[nt][kd], acc);
-      // lane (q, c): latent 16 (mt0 + m) + 4q .. +3 of row (nt, c)
       if (valid[nt]) {
-        u32x2 pk = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+        u32x2 pk = {pack_bf16x2(acc[nt][0], acc[nt][1]), pack_bf16x2(acc[nt][2], acc[nt][3])};
         *reinterpret_cast<u32x2*>(p.qcat + qrow[nt] * ROW + 16 * (mt0 + m) + 4 * q) = pk;
       }
     }
