@@ -23,6 +23,10 @@ CASES = [
     ("dsv3", 2, dict(batch=2, ctx=(1500, 33))),
     ("dsv3_g4", 1, dict(batch=3, ctx=(4096, 1000, 77))),
     ("dsv3_g4", 2, dict(batch=2, ctx=(1500, 33))),
+    # the smallest contexts the precondition s_q <= L allows (MTP row 0 of
+    # L = 2 sees one token), one page plus a token, and a batch of one
+    ("dsv3", 2, dict(batch=3, ctx=(2, 3, 65))),
+    ("dsv3", 1, dict(batch=1, ctx=1)),
 ]
 
 
