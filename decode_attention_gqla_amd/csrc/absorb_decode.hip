@@ -536,11 +536,13 @@ __global__ __launch_bounds__(512) void absorb_merge_kernel(DecodeParams p) {
   const int c = lane & 15, q = lane >> 4;
   // W_UV^T[G] operands of this wave's output tile md = w, loaded first so that
   // they arrive during the merge
+  // (the prologue stores W_UV^T[G] in operand order, so each load is one
+  // contiguous 1 KB block)
   const uint16_t* WT = p.wuvT + (size_t)G * DV * R;
   const int md = w < MD ? w : 0;
   bf16x8 wa[R / 32];
 #pragma unroll
-  for (int kk = 0; kk < R / 32; ++kk) wa[kk] = ld_bf16x8(WT + (size_t)(16 * md + c) * R + 32 * kk + 8 * q);
+  for (int kk = 0; kk < R / 32; ++kk) wa[kk] = ld_bf16x8(WT + ((size_t)(md * (R / 32) + kk) * 64 + lane) * 8);
 
   // ---- merge: wave w takes rows w, w + 8, ...; lane l holds latent 8l .. 8l+7
   // of the row (one coalesced 1 KB row per load instruction).  The loads (lse
@@ -756,9 +758,13 @@ __device__ __forceinline__ void absorb_q_block(const DecodeParams& p, int bx, in
   }
 }
 
-// W_UV[G] (r x d_v) -> W_UV^T[G] (d_v x r), through an LDS tile of 64 latent
-// rows x TD columns: 16-byte reads of W_UV rows, 2-byte transposed LDS
-// writes, 16-byte reads of LDS rows and 16-byte writes of W_UV^T rows.
+// W_UV[G] (r x d_v) -> W_UV^T[G] (d_v x r) in the merge's MFMA operand order,
+// through an LDS tile of 64 latent rows x TD columns: 16-byte reads of W_UV
+// rows, 2-byte transposed LDS writes, 16-byte reads of LDS rows.  The 8
+// latents l = 32 kk + 8 q .. +7 of output dim d = 16 md + c (the A operand of
+// lane 16 q + c in k step kk of output tile md) are stored as one 16-byte
+// chunk at element ((md * r / 32 + kk) * 64 + 16 q + c) * 8, so a wave's
+// operand load for one k step is one contiguous 1 KB block.
 template <int R, int DV>
 __device__ __forceinline__ void wuv_transpose_block(const DecodeParams& p, int bx, int by, int G) {
   constexpr int TD = DV < 64 ? DV : 64;              // columns per tile
@@ -775,7 +781,9 @@ __device__ __forceinline__ void wuv_transpose_block(const DecodeParams& p, int b
   __syncthreads();
   for (int e = tid; e < TD * 8; e += 256) {          // (column, 8 latent rows)
     const int d = e / 8, lc = (e % 8) * 8;
-    *reinterpret_cast<u32x4*>(p.wuvT + ((size_t)G * DV + d0 + d) * R + l0 + lc) =
+    const int dd = d0 + d, ll = l0 + lc;            // output dim, first of 8 latents
+    const size_t chunk = ((size_t)(dd / 16) * (R / 32) + ll / 32) * 64 + 16 * ((ll % 32) / 8) + dd % 16;
+    *reinterpret_cast<u32x4*>(p.wuvT + (size_t)G * DV * R + chunk * 8) =
         *reinterpret_cast<const u32x4*>(&t[d * TS + lc]);
   }
 }

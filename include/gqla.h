@@ -158,7 +158,8 @@ int gqla_append_tokens(const gqla_dims* d, int32_t batch, int32_t n_new, const v
  *            gqla_mqa_absorb_workspace_offsets) hold, after the call:
  *              [0] the absorbed query rows q_abs ++ q_rope, bf16
  *                  [batch][s_q][h_q][d_latent + d_rope];
- *              [1] W_UV transposed, bf16 [g][d_v][d_latent];
+ *              [1] W_UV transposed, bf16, g x d_v x d_latent elements (internal
+ *                  order: the merge's MFMA operand chunks);
  *              [2] the per-split normalised latent outputs o_lat, bf16
  *                  [units][s_q][h_q][d_latent] (units = total_splits under a
  *                  split plan, else batch with unit b = sequence b);
