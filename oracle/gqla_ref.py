@@ -432,16 +432,34 @@ def combine(part_out, part_lse, split_offsets):
 # ---------------------------------------------------------------------------
 # Acceptance metric used by the parity tests.
 # ---------------------------------------------------------------------------
+def _ratio(num: float, den: float) -> float:
+    """num / den for the acceptance ratios; a zero reference scale admits only a zero error."""
+    if den > 0:
+        return num / den
+    return 0.0 if num == 0 else math.inf
+
+
 def error_stats(got, ref) -> dict:
-    """max|err| / max|ref| and relative L2 of got against ref (float64)."""
+    """The acceptance metric of the parity tests, for got against ref (float64):
+
+      max_rel = max_i |got_i - ref_i| / max_i |ref_i|      (both maxima over all elements)
+      rel_l2  = ||got - ref||_2 / ||ref||_2                 (Euclidean norms, not squared)
+
+    so the bar max|err| <= tol * max|ref| reads max_rel <= tol.  With ref all zero the bar
+    admits only got == ref: the ratio is then 0 for a zero error and inf otherwise.  `finite`
+    is False when got holds a NaN or an infinity (max_rel and rel_l2 are then NaN or inf)."""
     got, ref = _f64(got), _f64(ref)
+    if got.shape != ref.shape:
+        raise ValueError(f"shape mismatch: {got.shape} vs {ref.shape}")
     err = got - ref
+    max_err = float(np.max(np.abs(err))) if err.size else 0.0
     max_ref = float(np.max(np.abs(ref))) if ref.size else 0.0
+    l2_err = float(np.linalg.norm(err.ravel()))
     l2_ref = float(np.linalg.norm(ref.ravel()))
     return {
-        "max_err": float(np.max(np.abs(err))) if err.size else 0.0,
+        "max_err": max_err,
         "max_ref": max_ref,
-        "max_rel": float(np.max(np.abs(err))) / max_ref if max_ref > 0 else 0.0,
-        "rel_l2": float(np.linalg.norm(err.ravel())) / l2_ref if l2_ref > 0 else 0.0,
+        "max_rel": _ratio(max_err, max_ref),
+        "rel_l2": _ratio(l2_err, l2_ref),
         "finite": bool(np.all(np.isfinite(got))),
     }
