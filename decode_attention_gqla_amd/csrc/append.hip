@@ -58,12 +58,16 @@ __global__ __launch_bounds__(256) void expand_tokens_kernel(AppendParams p) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c = lane & 15, q = lane >> 4;
   const int n_tok = p.batch * p.n_new;
-  // position of new token `tok` of the batch: its page and slot
-  auto locate = [&](int tok, int& page, int& slot) {
+  // position of new token `tok` of the batch: its page and slot; false when
+  // the position breaks the precondition (t < 0 or past the block table), and
+  // then nothing is written for the token
+  auto locate = [&](int tok, int& page, int& slot) -> bool {
     const int b = tok / p.n_new, j = tok % p.n_new;
-    const int t = max(p.seqlens[b] - p.n_new + j, 0);
-    page = p.block_table[(size_t)b * p.max_blocks + min(t / BS, p.max_blocks - 1)];
+    const int t = p.seqlens[b] - p.n_new + j;
+    if (t < 0 || t / BS >= p.max_blocks) return false;
+    page = p.block_table[(size_t)b * p.max_blocks + t / BS];
     slot = t % BS;
+    return true;
   };
   // this workgroup's column slice of W[G] into LDS by direct copy: piece
   // i * 64 + lane is row (i * 64 + lane) / PR, 16-byte piece % PR of the slice
@@ -106,9 +110,8 @@ __global__ __launch_bounds__(256) void expand_tokens_kernel(AppendParams p) {
   const size_t page_elems = (size_t)BS * (g * 2 * DH + DR);
   const int d0 = hsel * DC;                       // first output dim of this workgroup
   // lane (q, c) holds dims d0 + 16 mt + 4 q .. +3 of token c (K and V token-major)
-  if (tile * 16 + c < n_tok) {
-    int page_c, slot_c;
-    locate(tok_c, page_c, slot_c);
+  int page_c = 0, slot_c = 0;
+  if (tile * 16 + c < n_tok && locate(tok_c, page_c, slot_c)) {
     uint16_t* orow = p.expanded + (size_t)page_c * page_elems + (size_t)G * BS * 2 * DH + (kind_v ? BS * DH : 0) +
                      (size_t)slot_c * DH + d0;
 #pragma unroll

@@ -133,7 +133,9 @@ int gqla_expand_cache(const gqla_dims* d, const void* latent_pages, const void* 
  *             stays bit-identical to a full expansion of the latent cache; no
  *             other slot is written.
  * The latent rows are written before the expansion reads them (one stream).
- * Two new tokens must not share a slot. */
+ * Two new tokens must not share a slot.  A new token whose position is below 0
+ * (cache_seqlens[b] < n_new) or whose page index is >= max_blocks breaks the
+ * precondition; nothing is written for it, in either mode. */
 int gqla_append_tokens(const gqla_dims* d, int32_t batch, int32_t n_new, const void* new_rows,
                        void* latent_pages, int64_t num_pages, const int32_t* block_table,
                        int32_t max_blocks, const int32_t* cache_seqlens, const void* w_uk,

@@ -42,7 +42,7 @@ def test_absorb_decode_matches_oracle(name, s_q, kw):
     assert_lse_close(f64(lse), ref_l, "lse vs literal oracle")
 
 
-@pytest.mark.parametrize("split_tokens", [64, 1024])
+@pytest.mark.parametrize("split_tokens", [64, 1024, 2048])
 def test_absorb_split_kv_matches_oracle(split_tokens):
     log(f"absorb/split {split_tokens}")
     case = config_case("dsv3", 1, batch=3, ctx=(1500, 64, 2049), poison=True, table="random")
@@ -52,6 +52,19 @@ def test_absorb_split_kv_matches_oracle(split_tokens):
     ref_o, ref_l = decode_literal(*oracle_args(case), dims_of(case))
     assert_close(f64(out), ref_o, "split out vs oracle")
     assert_lse_close(f64(lse), ref_l, "split lse vs oracle")
+
+
+def test_absorb_bench_launch_configuration_full_context():
+    """The configuration the bench times: DeepSeek-V3 shape at context 4096 in 2048-token
+    splits, here over 8 sequences (every output row compared with the oracle)."""
+    log("absorb/dsv3 batch 8 ctx 4096 split 2048")
+    case = config_case("dsv3", 1, batch=8, poison=True, table="random")
+    gc = GpuCase(case)
+    out, lse = gc.absorb(split=gc.split(2048))
+    torch.cuda.synchronize()
+    ref_o, ref_l = decode_literal(*oracle_args(case), dims_of(case))
+    assert_close(f64(out), ref_o, "out vs literal oracle")
+    assert_lse_close(f64(lse), ref_l, "lse vs literal oracle")
 
 
 def test_absorb_ragged_long_context_sampled():

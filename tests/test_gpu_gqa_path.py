@@ -10,7 +10,8 @@ import torch
 import decode_attention_gqla_amd as G
 from decode_attention_gqla_amd.inputs import config_case, make_case, random_partials
 from oracle.gqla_ref import (bf16_round, combine, decode_gqa_expanded, decode_literal,
-                             expand_pages)
+                             expand_pages, expanded_offset_k, expanded_offset_rope,
+                             expanded_offset_v)
 from tests.gpu_util import GpuCase, assert_close, assert_lse_close, f64, log
 from tests.oracle_util import dims_of, oracle_args
 
@@ -235,6 +236,100 @@ def test_append_then_both_caches_equal_a_full_build(name, n_new):
     G.gqla_append_tokens(d, new_rows, start2, bt, sl)
     torch.cuda.synchronize()
     assert torch.equal(start2.view(torch.int16), full.view(torch.int16))
+
+
+def _selection_weights(case, seed):
+    """W_UK / W_UV with one 1.0 per column: the expansion becomes a pure gather."""
+    d = dims_of(case)
+    rng = np.random.default_rng(seed)
+    w_uk = torch.zeros_like(case.w_uk)
+    w_uv = torch.zeros_like(case.w_uv)
+    for g in range(d.g):
+        w_uk[g, torch.from_numpy(rng.choice(d.r, d.d_nope, replace=False)), torch.arange(d.d_nope)] = 1
+        w_uv[g, torch.from_numpy(rng.choice(d.r, d.d_v, replace=False)), torch.arange(d.d_v)] = 1
+    return w_uk, w_uv
+
+
+@pytest.mark.parametrize("weights", ["selection", "random"])
+def test_appended_slots_match_the_oracle_expansion(weights):
+    """The K, V and rope slots gqla_append_tokens writes for each sequence's last two tokens,
+    against oracle.expand_pages of the updated latent pages: bit-exact with selection weights
+    (a pure gather), within one bf16 ulp plus the fp32 accumulation bound with random weights.
+    Every other element of the expanded pool keeps its sentinel."""
+    n_new = 2
+    log(f"append vs oracle expansion, {weights} weights")
+    case = config_case("dsv3", 1, batch=4, ctx=(65, 4096, 1000, 129), poison=True, table="random")
+    if weights == "selection":
+        case.w_uk, case.w_uv = _selection_weights(case, seed=9)
+    d = dims_of(case)
+    dg = G.Dims.of(case)
+    dev = "cuda"
+    full = case.pages.to(dev)
+    bt, sl = case.block_table.to(dev), case.seqlens.to(dev)
+    w_uk, w_uv = case.w_uk.to(dev), case.w_uv.to(dev)
+    slots, rows = [], []
+    for b in range(case.batch):
+        L = int(case.seqlens[b])
+        for j in range(n_new):
+            t = L - n_new + j
+            slots.append((int(case.block_table[b, t // case.bs]), t % case.bs))
+            rows.append(full[slots[-1][0], slots[-1][1]].clone())
+    new_rows = torch.stack(rows).view(case.batch, n_new, -1).contiguous()
+    E = torch.full((full.shape[0], G.expanded_page_elems(dg)), 7.0, dtype=torch.bfloat16, device=dev)
+    G.gqla_append_tokens(dg, new_rows, full.clone(), bt, sl, w_uk, w_uv, expanded_pages=E)
+    torch.cuda.synchronize()
+    touched = sorted({pg for pg, _ in slots})
+    ref = expand_pages(f64(case.pages), f64(case.w_uk), f64(case.w_uv), d, page_ids=touched)
+    mag = expand_pages(np.abs(f64(case.pages)), np.abs(f64(case.w_uk)), np.abs(f64(case.w_uv)), d,
+                       page_ids=touched)
+    got = f64(E)
+    written = np.zeros(got.shape, dtype=bool)
+    for pg, slot in slots:
+        idx = []
+        for Gi in range(d.g):
+            idx += [expanded_offset_k(d, Gi, slot, j) for j in range(d.d_nope)]
+            idx += [expanded_offset_v(d, Gi, slot, j) for j in range(d.d_v)]
+        idx_rope = [expanded_offset_rope(d, slot, j) for j in range(d.d_R)]
+        r_pg = ref[touched.index(pg)]
+        g_pg = got[pg]
+        if weights == "selection":
+            assert np.array_equal(g_pg[idx], r_pg[idx]), (pg, slot)
+        else:
+            bound = _expected_ulp_bound(r_pg[idx]) + d.r * 2.0 ** -24 * mag[touched.index(pg)][idx] * 1.01
+            assert np.all(np.abs(g_pg[idx] - r_pg[idx]) <= bound), (pg, slot)
+        assert np.array_equal(g_pg[idx_rope], r_pg[idx_rope]), (pg, slot)
+        written[pg, idx + idx_rope] = True
+    assert np.all(got[~written] == 7.0)
+
+
+def test_append_skips_positions_outside_the_sequence_or_the_block_table():
+    """Tokens whose position falls before 0 (cache_seqlens < n_new) or past the block table
+    write nothing, in both modes; the one valid token rewrites its own row, so no slot of
+    either cache changes."""
+    n_new = 2
+    log("append with invalid positions")
+    case = config_case("dsv3", 1, batch=2, ctx=(1, 128), poison=True, table="random")
+    dg = G.Dims.of(case)
+    dev = "cuda"
+    assert case.max_blocks == 2
+    full = case.pages.to(dev)
+    bt = case.block_table.to(dev)
+    w_uk, w_uv = case.w_uk.to(dev), case.w_uv.to(dev)
+    E_full = G.expand_cache(dg, full, w_uk, w_uv)
+    # sequence 0: L = 1, so new token 0 sits at t = -1 (invalid) and token 1 at t = 0;
+    # sequence 1: L = 192 with a two-page table, so both new tokens sit on page index 2
+    sl = torch.tensor([1, 192], dtype=torch.int32, device=dev)
+    new_rows = torch.full((2, n_new, dg.d_latent + dg.d_rope), 9.0, dtype=torch.bfloat16, device=dev)
+    new_rows[0, 1] = full[int(case.block_table[0, 0]), 0]
+    lat = full.clone()
+    E = E_full.clone()
+    G.gqla_append_tokens(dg, new_rows, lat, bt, sl, w_uk, w_uv, expanded_pages=E)
+    lat2 = full.clone()
+    G.gqla_append_tokens(dg, new_rows, lat2, bt, sl)
+    torch.cuda.synchronize()
+    assert torch.equal(lat.view(torch.int16), full.view(torch.int16))
+    assert torch.equal(E.view(torch.int16), E_full.view(torch.int16))
+    assert torch.equal(lat2.view(torch.int16), full.view(torch.int16))
 
 
 def dims_of_gpu(case):
