@@ -32,6 +32,8 @@ WORKLOAD = ("DeepSeek-V3-shaped GQLA decode layer: 128 query heads, 8 groups, la
             "MQA-absorb s_q=1 over the latent cache + GQA s_q=2 over the expanded cache")
 SRC_FILES = ["decode_attention_gqla_amd/csrc/gqa_decode.hip",
              "decode_attention_gqla_amd/csrc/absorb_decode.hip",
+             "decode_attention_gqla_amd/csrc/absorb_wide.hip",
+             "decode_attention_gqla_amd/csrc/absorb_wide.hip.h",
              "decode_attention_gqla_amd/csrc/common.hip.h",
              "decode_attention_gqla_amd/csrc/combine.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")

@@ -14,7 +14,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgqla.so")
-SOURCES = ["gqla_api.hip", "gqa_decode.hip", "absorb_decode.hip", "expand.hip", "combine.hip", "select.hip", "append.hip"]
+SOURCES = ["gqla_api.hip", "gqa_decode.hip", "absorb_decode.hip", "absorb_wide.hip", "expand.hip", "combine.hip",
+           "select.hip", "append.hip"]
+# sources whose kernels keep MFMA accumulators in accumulation registers
+ACC_FORM: set[str] = set()
 ARCH = "gfx950"
 
 
@@ -25,17 +28,19 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libgqla)")
 
 
-def flags() -> list[str]:
-    return [
+def flags(src: str = "") -> list[str]:
+    f = [
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         # packed fp32 VALU forms are kept out of the generated code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        # MFMA accumulators in VGPRs: without it the GQA kernel copies its O
-        # tiles between VGPRs and AGPRs around every MFMA
-        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-I", os.path.join(ROOT, "include"), "-I", CSRC,
         "-Wno-unused-result",
     ]
+    if src not in ACC_FORM:
+        # MFMA accumulators in VGPRs: without it the GQA kernel copies its O
+        # tiles between VGPRs and AGPRs around every MFMA
+        f += ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+    return f
 
 
 def build(verbose: bool = False) -> str:
@@ -47,7 +52,7 @@ def build(verbose: bool = False) -> str:
     procs = []
     for src in SOURCES:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        cmd = [cc, *flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *flags(src), "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

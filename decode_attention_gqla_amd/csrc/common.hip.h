@@ -16,6 +16,7 @@ namespace gqla {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -163,6 +164,25 @@ __device__ __forceinline__ int sload_i32(const int32_t* ptr) {
   asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
   return v;
 }
+
+// Workgroup barrier for LDS hand-offs: this wave's LDS reads and writes are
+// complete before it arrives.
+__device__ __forceinline__ void block_sync_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Swizzle of 16-byte chunk positions inside a token row (tokens 0..31 of a
+// tile; requires 8 | chunks per row): the low three chunk bits are XOR-ed with
+// f(t) = 4 ((t >> 1) & 1) + 2 ((t >> 2) & 1).  gfx950 LDS has 64 four-byte
+// banks; a 16-byte read is served in four passes of 16 lanes (per half wave,
+// the 4-lane quads of even bit parity and those of odd parity), an 8-byte or
+// transposing read in two passes of 32 lanes.  With a 1152-byte token row
+// (token t starts at 16-byte slot 8 (t & 1) mod 16) this f makes every pass of
+// both readers hit 64 distinct banks: the QK reads (16 tokens x 4 consecutive
+// chunks per instruction) and the PV transposing reads (4 consecutive tokens x
+// 4 chunks per pass), checked exhaustively against that pass model over all
+// chunk offsets.
+__device__ __forceinline__ int tile_swz(int t) { return 4 * ((t >> 1) & 1) + 2 * ((t >> 2) & 1); }
 
 // Find the sequence owning split w: largest b with split_offsets[b] <= w.
 __device__ __forceinline__ int split_owner(const int32_t* __restrict__ offs, int batch, int w) {
