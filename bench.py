@@ -83,11 +83,13 @@ def copy_probe(nbytes: int):
     print(json.dumps({"copy_probe_bytes": n * 4, "dispatches": 3}))
 
 
-def cpu_baseline(case_abs, case_gqa, n_seqs: int):
+def cpu_baseline(case_abs, case_gqa, n_seqs: int, gpu_outs=None):
     """fp64 CPU oracle on a bounded sample: the literal decode of the first
-    n_seqs sequences on both paths' row sets."""
+    n_seqs sequences on both paths' row sets.  With gpu_outs ({path: (out, lse)}
+    as CPU tensors from the timed run) it also returns their parity against
+    these oracle outputs: error_stats of out and the largest lse error."""
     import numpy as np
-    from oracle.gqla_ref import Dims, decode_literal
+    from oracle.gqla_ref import Dims, decode_literal, error_stats
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
@@ -97,16 +99,32 @@ def cpu_baseline(case_abs, case_gqa, n_seqs: int):
     seqs = list(range(n_seqs))
     t0 = time.perf_counter()
     toks = 0
-    for case in (case_abs, case_gqa):
+    refs = {}
+    for name, case in (("mqa_absorb", case_abs), ("gqa", case_gqa)):
         d = Dims(h_q=case.h_q, g=case.g, r=case.r, d_R=case.d_R, d_nope=case.d_nope,
                  d_v=case.d_v, s_q=case.s_q, bs=case.bs)
-        decode_literal(f(case.q_nope), f(case.q_rope), f(case.pages), case.block_table.numpy(),
-                       case.seqlens.numpy(), f(case.w_uk), f(case.w_uv), d, seqs=seqs)
+        refs[name] = decode_literal(f(case.q_nope), f(case.q_rope), f(case.pages), case.block_table.numpy(),
+                                    case.seqlens.numpy(), f(case.w_uk), f(case.w_uv), d, seqs=seqs)
         toks += n_seqs * case.s_q
     dt = time.perf_counter() - t0
-    return {"value": toks / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"fp64 numpy literal decode (expand per group, then softmax attention) of "
-                      f"{n_seqs} of the 64 sequences on both paths ({toks} tokens, {dt:.1f} s)"}
+    cpu = {"value": toks / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+           "sample": f"fp64 numpy literal decode (expand per group, then softmax attention) of "
+                     f"{n_seqs} of the 64 sequences on both paths ({toks} tokens, {dt:.1f} s)"}
+    parity = None
+    if gpu_outs is not None:
+        parity = {"bar": {"max_rel": 1e-2, "rel_l2": 5e-3, "lse_abs": 2e-2},
+                  "sequences": n_seqs, "reference": "oracle decode_literal (fp64)"}
+        ok = True
+        for name, (out, lse) in gpu_outs.items():
+            ref_out, ref_lse = refs[name]
+            st = error_stats(f(out[:n_seqs]), ref_out)
+            lse_err = float(np.max(np.abs(f(lse[:n_seqs]) - ref_lse)))
+            good = bool(st["finite"] and st["max_rel"] <= 1e-2 and st["rel_l2"] <= 5e-3 and lse_err <= 2e-2)
+            ok = ok and good
+            parity[name] = {"max_rel": st["max_rel"], "rel_l2": st["rel_l2"], "lse_max_abs": lse_err,
+                            "pass": good}
+        parity["pass"] = ok
+    return cpu, parity
 
 
 def measure_append(G, d, pages, bt, sl, lens, w_uk, w_uv, E, steps: int, n_new: int = 2):
@@ -202,6 +220,88 @@ def measure_g4(G, rf, config_case, steps: int, absorb_split: int):
     return {"workload": "(g, s_q) = (4, 1): 128 query heads in 4 groups of 32, latent 512 + rope 64, "
                         "batch 64, context 4096", "absorb_split_tokens": absorb_split,
             "gqa_split_tokens": gsplit, "paths": res}
+
+
+def time_alternating(fns: dict, steps: int) -> dict:
+    """Median microseconds per call of each function, calling them in turn (each path's cache then
+    flushes the other's from the 256 MB memory-side cache, as in a step)."""
+    import torch
+    for _ in range(3):
+        for fn in fns.values():
+            fn()
+    torch.cuda.synchronize()
+    evs = {k: [] for k in fns}
+    for _ in range(steps):
+        for k, fn in fns.items():
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            evs[k].append((a, b))
+    torch.cuda.synchronize()
+    res = {}
+    for k in fns:
+        us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs[k])
+        res[k] = us[len(us) // 2]
+    return res
+
+
+def path_entry(us: float, tokens: int, w) -> dict:
+    return {"us_median": us, "tok_s": tokens / (us * 1e-6), "alg_bytes": w.bytes, "bound": w.bound(),
+            "achieved_GBps": w.bytes / (us * 1e-6) / 1e9, "roofline_us": w.roofline_us(),
+            "roofline_frac": w.roofline_us() / us}
+
+
+def measure_dense(G, rf, config_case, name: str, steps: int, absorb_split: int, gqa_split: int,
+                  sqs=((1, 2),), seed_base: int = 0) -> dict:
+    """Both decode paths on one config of `inputs.CONFIGS`: for each (absorb s_q, GQA s_q) pair the
+    MQA-absorb call over the latent cache and the GQA call over its expansion, split-KV by the
+    given partition sizes (0 = unsplit), timed alternately; the roofline of each call from the drawn
+    context lengths."""
+    import torch
+    res = {}
+    E = None
+    for sq_a, sq_g in sqs:
+        # one seed for every pair, so the cache (and its expansion) is the same
+        ca = config_case(name, sq_a, seed=seed_base + 10)
+        cg = config_case(name, sq_g, seed=seed_base + 10)
+        assert torch.equal(ca.pages, cg.pages) and torch.equal(ca.w_uv, cg.w_uv)
+        dev = "cuda"
+        da, dg = G.Dims.of(ca), G.Dims.of(cg)
+        pages, bt, sl = ca.pages.to(dev), ca.block_table.to(dev), ca.seqlens.to(dev)
+        w_uk, w_uv = ca.w_uk.to(dev), ca.w_uv.to(dev)
+        if E is None:
+            E = G.expand_cache(dg, pages, w_uk, w_uv)
+        qa = (ca.q_nope.to(dev), ca.q_rope.to(dev))
+        qg = (cg.q_nope.to(dev), cg.q_rope.to(dev))
+        B, H = ca.batch, ca.h_q
+        lens = [int(x) for x in ca.seqlens]
+        out_a = torch.empty(B, sq_a, H, ca.d_v, dtype=torch.bfloat16, device=dev)
+        lse_a = torch.empty(B, sq_a, H, dtype=torch.float32, device=dev)
+        out_g = torch.empty(B, sq_g, H, cg.d_v, dtype=torch.bfloat16, device=dev)
+        lse_g = torch.empty(B, sq_g, H, dtype=torch.float32, device=dev)
+        sa = G.make_split_plan(lens, absorb_split) if absorb_split else (None, 0)
+        sg = G.make_split_plan(lens, gqa_split) if gqa_split else (None, 0)
+        ws = G.absorb_workspace(da, B, total_splits=sa[1])
+        po = torch.empty(sg[1], sq_g, H, cg.d_v, dtype=torch.float32, device=dev) if gqa_split else None
+        pl = torch.empty(sg[1], sq_g, H, dtype=torch.float32, device=dev) if gqa_split else None
+        fns = {
+            "mqa_absorb": lambda: G.gqla_decode_mqa_absorb(da, qa[0], qa[1], pages, bt, sl, w_uk, w_uv, out=out_a,
+                                                           lse=lse_a, split_offsets=sa[0],
+                                                           split_tokens=absorb_split if absorb_split else 0,
+                                                           total_splits=sa[1], workspace=ws),
+            "gqa": lambda: G.gqla_decode_gqa(dg, qg[0], qg[1], E, bt, sl, out=out_g, lse=lse_g, split_offsets=sg[0],
+                                             split_tokens=gqa_split if gqa_split else 0, total_splits=sg[1],
+                                             part_out=po, part_lse=pl),
+        }
+        us = time_alternating(fns, steps)
+        wa = rf.work_absorb(lens, H, ca.g, ca.r, ca.d_R, ca.d_nope, ca.d_v, sq_a)
+        wg = rf.work_gqa(lens, H, cg.g, cg.d_R, cg.d_nope, cg.d_v, sq_g)
+        res[f"absorb_sq{sq_a}"] = path_entry(us["mqa_absorb"], B * sq_a, wa)
+        res[f"gqa_sq{sq_g}"] = path_entry(us["gqa"], B * sq_g, wg)
+        del pages
+    del E
+    return res
 
 
 def measure_sparse(G, rf, d2, qn, qr, E, bt, sl, lens, steps: int, topks=(2048, 512)):
@@ -414,15 +514,23 @@ def main():
                 traffic = ent.get("bytes_per_launch")
         except Exception:  # pragma: no cover
             traffic = None
-    if wd.bound() == "hbm":
-        roof = {"bound": "hbm", "achieved": wd.bytes / (td * 1e-6) / 1e9, "peak": rf.MI355X_HBM_GBPS,
-                "unit": "GB/s"}
-    else:
-        roof = {"bound": "mfma", "achieved": wd.flops / (td * 1e-6) / 1e12,
-                "peak": rf.MI355X_BF16_TFLOPS, "unit": "TFLOP/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
+    def roof_of(w, t):
+        if w.bound() == "hbm":
+            r = {"bound": "hbm", "achieved": w.bytes / (t * 1e-6) / 1e9, "peak": rf.MI355X_HBM_GBPS,
+                 "unit": "GB/s"}
+        else:
+            r = {"bound": "mfma", "achieved": w.flops / (t * 1e-6) / 1e12,
+                 "peak": rf.MI355X_BF16_TFLOPS, "unit": "TFLOP/s"}
+        r["frac"] = r["achieved"] / r["peak"]
+        return r
+    roof = roof_of(wd, td)
     roof["traffic"] = traffic
     roof["kernel"] = dom
+    # every path's own fraction, and whether each reaches 70% of its roofline
+    roof["per_path"] = {n: roof_of(works[n][0], per_path[n]["us_mean"]) for n, _ in paths}
+    roof["target_frac"] = 0.7
+    roof["target_met"] = all(v["frac"] >= 0.7 for v in roof["per_path"].values())
+    roof["worst_path"] = min(roof["per_path"], key=lambda n: roof["per_path"][n]["frac"])
     # the path selector on this batch: at the roofline, and with the fractions of it that
     # each path just reached here
     selector = None
@@ -445,10 +553,23 @@ def main():
                     "sparse_gqa": measure_sparse(G, rf, d2, qg_n, qg_r, E, bt, sl, lens, args.steps),
                     "sparse_gqa_ragged": measure_sparse_ragged(G, rf, config_case, args.steps),
                     "g4_sq1": measure_g4(G, rf, config_case, args.steps, args.absorb_split)}
+        log("variants: dense ragged long-context mix, LLaMA-3-8B shape")
+        variants["dense_ragged"] = {
+            "workload": "ragged long-context mix: DeepSeek-V3 shape, 16 sequences, contexts log-uniform in "
+                        "[1024, 32768], random 64-token page table; absorb s_q = 1 and GQA s_q = 2, split-KV",
+            "absorb_split_tokens": 1024, "gqa_split_tokens": 1024,
+            "paths": measure_dense(G, rf, config_case, "dsv3_ragged", args.steps, 1024, 1024, ((1, 2),), 1004)}
+        variants["llama3_8b"] = {
+            "workload": "LLaMA-3-8B-shaped layer: 32 query heads, 8 groups, latent 512 + rope 64, nope/v 128, "
+                        "batch 32, context 2048; both paths at s_q = 1 and s_q = 2",
+            "absorb_split_tokens": 256, "gqa_split_tokens": 256,
+            "paths": measure_dense(G, rf, config_case, "llama3_8b", args.steps, 256, 256, ((1, 1), (2, 2)), 1001)}
     cpu = None
+    parity = None
     if not args.no_cpu and not args.only:
-        log("cpu oracle baseline")
-        cpu = cpu_baseline(case_abs, case_gqa, args.cpu_seqs)
+        log("cpu oracle baseline and parity of the timed outputs")
+        gpu_outs = {"mqa_absorb": (out_a.cpu(), lse_a.cpu()), "gqa": (out_g.cpu(), lse_g.cpu())}
+        cpu, parity = cpu_baseline(case_abs, case_gqa, args.cpu_seqs, gpu_outs)
     line = {
         "metric": METRIC,
         "value": tokens / (ms_step * 1e-3),
@@ -462,6 +583,7 @@ def main():
                    "only": args.only},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "parity": parity,
         "paths": per_path,
         "expand_us": t_expand_us,
         "path_selector": selector,

@@ -93,6 +93,9 @@ _SIGS = {
                                         ctypes.c_uint64),
     "gqla_mqa_absorb_workspace_offsets": ([ctypes.POINTER(Dims), ctypes.c_int32, ctypes.c_int32,
                                            ctypes.POINTER(ctypes.c_uint64)], ctypes.c_int),
+    "gqla_mqa_absorb_merge": ([ctypes.POINTER(Dims), ctypes.c_int32, _vp, _f32p, _i32p, ctypes.c_int32, _vp,
+                               _vp, _f32p, _vp, ctypes.c_uint64, _vp], ctypes.c_int),
+    "gqla_mqa_absorb_merge_workspace_bytes": ([ctypes.POINTER(Dims)], ctypes.c_uint64),
     "gqla_decode_gqa": ([ctypes.POINTER(Dims), ctypes.c_int32, _vp, _vp, _vp, _i32p,
                          ctypes.c_int32, _i32p, _i32p, ctypes.c_int32, ctypes.c_int32, _vp,
                          _f32p, _f32p, _f32p, _vp], ctypes.c_int),
@@ -226,6 +229,31 @@ def gqla_mqa_absorb_workspace_offsets(d: Dims, batch: int, total_splits: int = 0
     _check(lib().gqla_mqa_absorb_workspace_offsets(ctypes.byref(d), int(batch), int(total_splits),
                                                    off), "gqla_mqa_absorb_workspace_offsets")
     return [int(x) for x in off]
+
+
+def gqla_mqa_absorb_merge_workspace_bytes(d: Dims) -> int:
+    return int(lib().gqla_mqa_absorb_merge_workspace_bytes(ctypes.byref(d)))
+
+
+def gqla_mqa_absorb_merge(d: Dims, part_lat, part_lse, w_uv, out, lse=None, split_offsets=None,
+                          total_splits=0, workspace=None, stream=None) -> None:
+    """Latent-space merge of absorb split partials and the up-projection by W_UV[G]."""
+    B = out.shape[0]
+    units = total_splits if split_offsets is not None else B
+    rows = (d.s_q, d.num_heads)
+    pl = _ptr(part_lat, torch.bfloat16, "part_lat", (units,) + rows + (d.d_latent,))
+    pe = _ptr(part_lse, torch.float32, "part_lse", (units,) + rows)
+    so = _ptr(split_offsets, torch.int32, "split_offsets", (B + 1,), allow_none=True)
+    wv = _ptr(w_uv, torch.bfloat16, "w_uv", (d.num_groups, d.d_latent, d.d_v))
+    o = _ptr(out, torch.bfloat16, "out", (B,) + rows + (d.d_v,))
+    ls = _ptr(lse, torch.float32, "lse", (B,) + rows, allow_none=True)
+    if workspace is None:
+        workspace = torch.empty(max(gqla_mqa_absorb_merge_workspace_bytes(d), 16), dtype=torch.uint8,
+                                device=out.device)
+    ws = _ptr(workspace, torch.uint8, "workspace")
+    st = lib().gqla_mqa_absorb_merge(ctypes.byref(d), B, pl, pe, so, int(total_splits), wv, o, ls, ws,
+                                     int(workspace.numel()), _stream(stream))
+    _check(st, "gqla_mqa_absorb_merge")
 
 
 def gqla_decode_mqa_absorb(d: Dims, q_nope, q_rope, latent_pages, block_table, cache_seqlens,

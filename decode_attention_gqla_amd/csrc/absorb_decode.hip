@@ -797,6 +797,14 @@ __global__ __launch_bounds__(256) void absorb_prologue_kernel(DecodeParams p, in
   }
 }
 
+template <int HPG, int SQ, int R, int DV>
+hipError_t launch_merge(const DecodeParams& p, hipStream_t stream) {
+  constexpr int RG = HPG * SQ, SB = RG >= 32 ? 1 : 32 / RG, RCH = RG > 32 ? RG / 32 : 1;
+  dim3 grid((unsigned)((p.batch + SB - 1) / SB * RCH), (unsigned)p.num_groups);
+  hipLaunchKernelGGL((absorb_merge_kernel<HPG, SQ, R, DV>), grid, dim3(512), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <int HPG, int SQ, int R, int DR, int DN, int DV>
 hipError_t launch_absorb(const DecodeParams& p, hipStream_t stream) {
   using C = AbsorbCfg<HPG, SQ, R, DR, DN, DV>;
@@ -827,18 +835,31 @@ hipError_t launch_absorb(const DecodeParams& p, hipStream_t stream) {
     }
     if (e != hipSuccess) return e;
   }
-  constexpr int RG = HPG * SQ, SB = RG >= 32 ? 1 : 32 / RG, RCH = RG > 32 ? RG / 32 : 1;
-  dim3 grid((unsigned)((p.batch + SB - 1) / SB * RCH), (unsigned)p.num_groups);
-  hipLaunchKernelGGL((absorb_merge_kernel<HPG, SQ, R, DV>), grid, dim3(512), 0, stream, p);
-  return hipGetLastError();
+  return launch_merge<HPG, SQ, R, DV>(p, stream);
 }
 
+// The merge and up-projection alone, over caller-provided latent partials
+// (p.olat, p.olse, p.split_offsets): W_UV^T first (the prologue launch with
+// no q_abs blocks), then the merge.
+template <int HPG, int SQ, int R, int DR, int DN, int DV>
+hipError_t launch_absorb_merge(const DecodeParams& p, hipStream_t stream) {
+  constexpr int TD = DV < 64 ? DV : 64;
+  const int nt = (R / 64) * (DV / TD) * p.num_groups;
+  hipLaunchKernelGGL((absorb_prologue_kernel<HPG, SQ, R, DR, DN, DV>), dim3((unsigned)nt), dim3(256), 0, stream, p,
+                     0, 1);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_merge<HPG, SQ, R, DV>(p, stream);
+}
+
+// merge_only: the merge and up-projection of caller-provided partials.
 hipError_t absorb_dispatch(int hpg, int sq, int r, int dn, int dv, int dr, const DecodeParams& p,
-                           hipStream_t stream, bool* supported) {
+                           hipStream_t stream, bool* supported, bool merge_only) {
   *supported = true;
 #define GQLA_ABS_CASE(HPG, SQ, R, DR, DN, DV)                                     \
-  if (hpg == HPG && sq == SQ && r == R && dr == DR && dn == DN && dv == DV) \
-    return launch_absorb<HPG, SQ, R, DR, DN, DV>(p, stream);
+  if (hpg == HPG && sq == SQ && r == R && dr == DR && dn == DN && dv == DV)  \
+    return merge_only ? launch_absorb_merge<HPG, SQ, R, DR, DN, DV>(p, stream) \
+                      : launch_absorb<HPG, SQ, R, DR, DN, DV>(p, stream);
   GQLA_ABS_CASE(16, 1, 512, 64, 128, 128)
   GQLA_ABS_CASE(16, 2, 512, 64, 128, 128)
   GQLA_ABS_CASE(32, 1, 512, 64, 128, 128)

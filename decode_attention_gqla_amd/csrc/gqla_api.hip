@@ -12,7 +12,7 @@ namespace gqla {
 hipError_t gqa_dispatch(int hpg, int sq, int dn, int dv, int dr, const DecodeParams& p,
                         hipStream_t stream, bool* supported);
 hipError_t absorb_dispatch(int hpg, int sq, int r, int dn, int dv, int dr, const DecodeParams& p,
-                           hipStream_t stream, bool* supported);
+                           hipStream_t stream, bool* supported, bool merge_only);
 hipError_t expand_dispatch(int r, int dn, int dv, int dr, const ExpandParams& p, hipStream_t stream,
                            bool* supported);
 hipError_t combine_dispatch(int dv, const CombineParams& p, hipStream_t stream, bool* supported);
@@ -293,7 +293,38 @@ int gqla_decode_mqa_absorb(const gqla_dims* d, int32_t batch, const void* q_nope
   p.olse = (float*)((char*)workspace + off[3]);
   bool ok = true;
   hipError_t e = gqla::absorb_dispatch(d->num_heads / d->num_groups, d->s_q, d->d_latent,
-                                       d->d_nope, d->d_v, d->d_rope, p, (hipStream_t)stream, &ok);
+                                       d->d_nope, d->d_v, d->d_rope, p, (hipStream_t)stream, &ok, false);
+  return finish(e, ok);
+}
+
+uint64_t gqla_mqa_absorb_merge_workspace_bytes(const gqla_dims* d) {
+  if (!d || d->num_groups <= 0 || d->d_v <= 0 || d->d_latent <= 0) return 0;
+  return ((uint64_t)d->num_groups * d->d_v * (uint64_t)d->d_latent * 2u + 255u) & ~(uint64_t)255u;
+}
+
+int gqla_mqa_absorb_merge(const gqla_dims* d, int32_t batch, const void* part_lat, const float* part_lse,
+                          const int32_t* split_offsets, int32_t total_splits, const void* w_uv, void* out,
+                          float* lse, void* workspace, uint64_t workspace_bytes, void* stream) {
+  int st = check_dims(d);
+  if (st != GQLA_OK) return st;
+  if (batch < 0) return GQLA_ERR_INVALID_ARG;
+  if (split_offsets && total_splits < batch) return GQLA_ERR_BAD_SPLIT_PLAN;
+  if (!part_lat || !part_lse || !w_uv || !out) return GQLA_ERR_INVALID_ARG;
+  if (!aligned16(part_lat) || !aligned4(part_lse) || !aligned16(w_uv) || !aligned16(out) ||
+      (lse && !aligned4(lse)) || (split_offsets && !aligned4(split_offsets)))
+    return GQLA_ERR_MISALIGNED;
+  if (!workspace || workspace_bytes < gqla_mqa_absorb_merge_workspace_bytes(d)) return GQLA_ERR_INVALID_ARG;
+  if (!aligned16(workspace)) return GQLA_ERR_MISALIGNED;
+  if (batch == 0) return GQLA_OK;
+  gqla::DecodeParams p = make_params(d, batch, nullptr, nullptr, nullptr, nullptr, 1, nullptr, nullptr, w_uv,
+                                     split_offsets, 0, split_offsets ? total_splits : batch, out, lse, nullptr,
+                                     nullptr);
+  p.wuvT = (uint16_t*)workspace;
+  p.olat = (uint16_t*)part_lat;
+  p.olse = (float*)part_lse;
+  bool ok = true;
+  hipError_t e = gqla::absorb_dispatch(d->num_heads / d->num_groups, d->s_q, d->d_latent, d->d_nope, d->d_v,
+                                       d->d_rope, p, (hipStream_t)stream, &ok, true);
   return finish(e, ok);
 }
 

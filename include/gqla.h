@@ -189,6 +189,40 @@ uint64_t gqla_mqa_absorb_workspace_bytes(const gqla_dims* d, int32_t batch, int3
 int gqla_mqa_absorb_workspace_offsets(const gqla_dims* d, int32_t batch, int32_t total_splits,
                                       uint64_t* offsets);
 
+/* Merge of MQA-absorb split partials in the latent space, then the
+ * up-projection (paperlayer.ai section 4, "MQA-absorb path": attention runs
+ * over the latent and W_UV[G] maps its output back; the up-projection is
+ * linear, so the splits may be merged before it).  For each query row
+ * (b, i, h) of group G = h / (h_q / g), over the units s of sequence b:
+ *   m = max_s lse_s,  w_s = exp(lse_s - m),  o = sum_s w_s part_lat_s / sum_s w_s,
+ *   lse = m + ln sum_s w_s,  out = o W_UV[G]   (fp32 throughout, bf16 out).
+ *   part_lat   bf16 [units][s_q][h_q][d_latent]: each split's normalised
+ *              latent output;
+ *   part_lse   fp32 [units][s_q][h_q]; -inf marks a split that saw no token
+ *              of the row (its part_lat row then carries weight 0);
+ *   split_offsets  int32 [batch + 1] or NULL: sequence b owns units
+ *              split_offsets[b] .. split_offsets[b + 1] - 1; NULL means unit b
+ *              is sequence b (units = batch);
+ *   total_splits   units when split_offsets is given (>= batch, else
+ *              GQLA_ERR_BAD_SPLIT_PLAN); ignored otherwise;
+ *   w_uv       bf16 [g][d_latent][d_v];
+ *   out        bf16 [batch][s_q][h_q][d_v];  lse fp32 [batch][s_q][h_q] or NULL;
+ *   workspace  at least gqla_mqa_absorb_merge_workspace_bytes(d) bytes of
+ *              device scratch, 16-byte aligned, owned by the caller (W_UV
+ *              transposed); too small or NULL returns GQLA_ERR_INVALID_ARG.
+ * part_lat and part_lse have the layouts of regions [2] and [3] of the
+ * gqla_decode_mqa_absorb workspace, so this call also re-merges the partials a
+ * decode call left there.  A row whose units all have lse = -inf gets out = 0
+ * and lse = -inf.  The same checks as the decode calls run on the host before
+ * anything is enqueued; batch = 0 is a no-op. */
+int gqla_mqa_absorb_merge(const gqla_dims* d, int32_t batch, const void* part_lat, const float* part_lse,
+                          const int32_t* split_offsets, int32_t total_splits, const void* w_uv, void* out,
+                          float* lse, void* workspace, uint64_t workspace_bytes, void* stream);
+
+/* Bytes of workspace gqla_mqa_absorb_merge needs; 0 for d == NULL or
+ * non-positive g, d_v or d_latent. */
+uint64_t gqla_mqa_absorb_merge_workspace_bytes(const gqla_dims* d);
+
 /* GQA decode over the per-group expanded cache (paperlayer.ai section 4,
  * "GQA path"; gist.science section 2 "GQA-Pfad": conventional grouped-query
  * attention with no per-step latent expansion).  Arguments as for

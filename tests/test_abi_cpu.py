@@ -221,3 +221,28 @@ def test_binding_rejects_cpu_tensors_and_wrong_dtypes(lib):
 def test_split_plan_counts_ceil_per_sequence():
     offs, total = G.make_split_plan([1, 1024, 1025, 4096], 1024, device="cpu")
     assert offs.tolist() == [0, 1, 2, 4, 8] and total == 8
+
+
+def merge(lib, d, batch=1, part=A, plse=A, split=None, total=0, wuv=A, out=A, lse=None, ws=A, ws_bytes=1 << 40):
+    return lib.gqla_mqa_absorb_merge(ctypes.byref(d) if d is not None else None, batch, part, plse, split, total,
+                                     wuv, out, lse, ws, ws_bytes, None)
+
+
+def test_absorb_merge_rejects_bad_arguments_on_the_host(lib):
+    d = dsv3()
+    need = lib.gqla_mqa_absorb_merge_workspace_bytes(ctypes.byref(d))
+    assert need == 8 * 128 * 512 * 2                  # W_UV transposed, bf16
+    assert lib.gqla_mqa_absorb_merge_workspace_bytes(None) == 0
+    assert merge(lib, None) == INVALID
+    assert merge(lib, d, batch=-1) == INVALID
+    for kw in (dict(part=None), dict(plse=None), dict(wuv=None), dict(out=None), dict(ws=None)):
+        assert merge(lib, d, **kw) == INVALID, kw
+    for kw in (dict(part=ODD), dict(wuv=ODD), dict(out=ODD), dict(ws=ODD),
+               dict(plse=ctypes.c_void_p(0x10002)), dict(lse=ctypes.c_void_p(0x10002)),
+               dict(split=ctypes.c_void_p(0x10002), total=4)):
+        assert merge(lib, d, **kw) == MISALIGNED, kw
+    assert merge(lib, d, batch=3, split=A, total=2) == BADSPLIT
+    assert merge(lib, d, ws_bytes=need - 1) == INVALID
+    bad = dsv3(d_v=96)
+    assert merge(lib, bad) == UNSUPPORTED
+    assert merge(lib, d, batch=0) == OK               # nothing to do, nothing enqueued

@@ -207,3 +207,69 @@ def test_absorb_partials_match_oracle_partials():
     assert np.all(got_lat[empty] == 0)
     assert_close(got_lat[~empty], ref_lat[~empty], "latent partials")
     assert_lse_close(got_lse[~empty], ref_lse[~empty], "partial lse")
+
+
+@pytest.mark.parametrize("name,s_q,split", [("dsv3", 2, 256), ("dsv3", 1, 1024), ("llama3_8b", 1, 64),
+                                            ("tiny", 2, None)])
+def test_merge_entry_point_on_oracle_latent_partials(name, s_q, split):
+    """gqla_mqa_absorb_merge on latent partials computed by the oracle (rounded to bf16, the
+    entry point's input type): against the oracle's log-sum-exp combine of the same rounded
+    partials followed by the up-projection by W_UV[G], and against the literal decode."""
+    from oracle.gqla_ref import combine, decode_partials_latent
+    log(f"absorb/merge entry {name} s_q={s_q} split={split}")
+    kw = dict(batch=3, ctx=(700, 130, 65)) if name != "tiny" else dict()
+    case = config_case(name, s_q, poison=True, table="random", **kw)
+    d = dims_of(case)
+    gd = G.Dims.of(case)
+    args = oracle_args(case)
+    q_nope, q_rope, pages, bt, sl, w_uk, w_uv = args
+    lens = [int(x) for x in case.seqlens]
+    B = len(lens)
+    split_tokens = split if split else max(lens) + 64 - max(lens) % 64
+    ref_lat, ref_lse, ref_off = decode_partials_latent(q_nope, q_rope, pages, bt, sl, w_uk, d, split_tokens)
+    lat_bf = torch.from_numpy(ref_lat).to(torch.bfloat16)
+    lse_f = torch.from_numpy(ref_lse).to(torch.float32)
+    total = int(ref_off[-1])
+    out = torch.empty(B, s_q, case.h_q, case.d_v, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(B, s_q, case.h_q, dtype=torch.float32, device="cuda")
+    offs = torch.tensor(ref_off, dtype=torch.int32, device="cuda") if split else None
+    G.gqla_mqa_absorb_merge(gd, lat_bf.cuda(), lse_f.cuda(), case.w_uv.cuda(), out, lse=lse,
+                            split_offsets=offs, total_splits=total if split else 0)
+    torch.cuda.synchronize()
+    # oracle: combine the rounded partials, then o W_UV[G] per group
+    m_lat, m_lse = combine(lat_bf.double().numpy(), lse_f.double().numpy(), ref_off)
+    hpg = case.h_q // case.g
+    w = np.repeat(w_uv, hpg, axis=0)                     # [h_q][d_latent][d_v], head h -> group h // hpg
+    ref_out = np.einsum("bihl,hlv->bihv", m_lat, w)
+    assert_close(f64(out), ref_out, "merge vs oracle combine + up-projection")
+    fin = np.isfinite(m_lse)
+    assert np.array_equal(fin, np.isfinite(f64(lse)))
+    assert_lse_close(f64(lse)[fin], m_lse[fin], "merge lse vs oracle combine")
+    lit_o, _ = decode_literal(*args, d)
+    assert_close(f64(out), lit_o, "merge vs literal decode")
+
+
+def test_merge_entry_point_remerges_the_decode_workspace():
+    """The partials a decode call leaves in its workspace, merged again by the entry point,
+    give the decode call's own output bit for bit (the same merge kernel)."""
+    log("absorb/merge entry over the decode workspace")
+    case = config_case("dsv3", 1, batch=3, ctx=(1500, 64, 2049), poison=True, table="random")
+    gc = GpuCase(case)
+    d = gc.d
+    offs, total, st = gc.split(1024)
+    ws = G.absorb_workspace(d, 3, total_splits=total)
+    out = torch.empty(3, 1, d.num_heads, d.d_v, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(3, 1, d.num_heads, dtype=torch.float32, device="cuda")
+    G.gqla_decode_mqa_absorb(d, gc.q_nope, gc.q_rope, gc.pages, gc.block_table, gc.seqlens, gc.w_uk, gc.w_uv,
+                             out=out, lse=lse, split_offsets=offs, split_tokens=st, total_splits=total,
+                             workspace=ws)
+    o0, o1, o2, o3 = G.gqla_mqa_absorb_workspace_offsets(d, 3, total)
+    rows = d.s_q * d.num_heads
+    lat = ws[o2:o2 + total * rows * d.d_latent * 2].view(torch.bfloat16).view(total, 1, d.num_heads, d.d_latent)
+    plse = ws[o3:o3 + total * rows * 4].view(torch.float32).view(total, 1, d.num_heads)
+    out2 = torch.empty_like(out)
+    lse2 = torch.empty_like(lse)
+    G.gqla_mqa_absorb_merge(d, lat.clone(), plse.clone(), gc.w_uv, out2, lse=lse2, split_offsets=offs,
+                            total_splits=total)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
