@@ -28,7 +28,9 @@ LIB_PATH = os.path.join(_HERE, "libgqla.so")
 
 GQLA_OK = 0
 STATUS_NAMES = {0: "GQLA_OK", -1: "GQLA_ERR_INVALID_ARG", -2: "GQLA_ERR_UNSUPPORTED_SHAPE",
-                -3: "GQLA_ERR_MISALIGNED", -4: "GQLA_ERR_BAD_SPLIT_PLAN", -5: "GQLA_ERR_HIP"}
+                -3: "GQLA_ERR_MISALIGNED", -4: "GQLA_ERR_BAD_SPLIT_PLAN", -5: "GQLA_ERR_HIP",
+                -6: "GQLA_ERR_SCRATCH_LIMIT"}
+NOALLOC_SCRATCH_BYTES = 32 << 20       # GQLA_NOALLOC_SCRATCH_BYTES
 
 
 class GqlaError(RuntimeError):
@@ -93,6 +95,9 @@ _SIGS = {
                                         ctypes.c_uint64),
     "gqla_mqa_absorb_workspace_offsets": ([ctypes.POINTER(Dims), ctypes.c_int32, ctypes.c_int32,
                                            ctypes.POINTER(ctypes.c_uint64)], ctypes.c_int),
+    "gqla_decode_mqa_absorb_noalloc": ([ctypes.POINTER(Dims), ctypes.c_int32, _vp, _vp, _vp, _i32p,
+                                        ctypes.c_int32, _i32p, _vp, _vp, _i32p, ctypes.c_int32,
+                                        ctypes.c_int32, _vp, _f32p, _vp], ctypes.c_int),
     "gqla_mqa_absorb_merge": ([ctypes.POINTER(Dims), ctypes.c_int32, _vp, _f32p, _i32p, ctypes.c_int32, _vp,
                                _vp, _f32p, _vp, ctypes.c_uint64, _vp], ctypes.c_int),
     "gqla_mqa_absorb_merge_workspace_bytes": ([ctypes.POINTER(Dims)], ctypes.c_uint64),
@@ -229,6 +234,21 @@ def gqla_mqa_absorb_workspace_offsets(d: Dims, batch: int, total_splits: int = 0
     _check(lib().gqla_mqa_absorb_workspace_offsets(ctypes.byref(d), int(batch), int(total_splits),
                                                    off), "gqla_mqa_absorb_workspace_offsets")
     return [int(x) for x in off]
+
+
+def gqla_decode_mqa_absorb_noalloc(d: Dims, q_nope, q_rope, latent_pages, block_table, cache_seqlens,
+                                   w_uk, w_uv, out=None, lse=None, split_offsets=None, split_tokens=0,
+                                   total_splits=0, stream=None) -> None:
+    """gqla_decode_mqa_absorb with the library's fixed scratch array as its workspace."""
+    B, mb, a = _decode_common(d, q_nope, q_rope, block_table, cache_seqlens, split_offsets,
+                              total_splits, out, lse, None, None)
+    st = lib().gqla_decode_mqa_absorb_noalloc(
+        ctypes.byref(d), B, a["q_nope"], a["q_rope"],
+        _ptr(latent_pages, torch.bfloat16, "latent_pages"), a["block_table"], mb, a["seqlens"],
+        _ptr(w_uk, torch.bfloat16, "w_uk", (d.num_groups, d.d_latent, d.d_nope)),
+        _ptr(w_uv, torch.bfloat16, "w_uv", (d.num_groups, d.d_latent, d.d_v)),
+        a["split_offsets"], int(split_tokens), int(total_splits), a["out"], a["lse"], _stream(stream))
+    _check(st, "gqla_decode_mqa_absorb_noalloc")
 
 
 def gqla_mqa_absorb_merge_workspace_bytes(d: Dims) -> int:

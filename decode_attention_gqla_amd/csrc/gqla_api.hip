@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/gqla.h"
 #include "common.hip.h"
 #include "params.hip.h"
@@ -20,7 +22,41 @@ hipError_t append_launch(const AppendParams& p, int r, int dn, int dv, int dr, h
 hipError_t sparse_codes_launch(const SparseCodeParams& p, hipStream_t stream);
 }  // namespace gqla
 
+// Workspace of gqla_decode_mqa_absorb_noalloc: one copy per GPU, kept until
+// the process ends.  Host code never uses the name itself (on the host it is a
+// stand-in, not a device address): the device address comes from
+// hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[GQLA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];                 // device address of `scratch`, per device
+
+// The current device's copy of `scratch`, looked up on the first call with
+// that device current.
+hipError_t scratch_of_current_device(hipStream_t stream, void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (stream) {
+    hipDevice_t sdev = 0;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return e;
+    if ((int)sdev != dev) return hipErrorInvalidDevice;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
@@ -153,6 +189,7 @@ const char* gqla_status_string(int status) {
     case GQLA_ERR_MISALIGNED: return "GQLA_ERR_MISALIGNED: tensor pointers must be 16-byte aligned (index arrays 4-byte)";
     case GQLA_ERR_BAD_SPLIT_PLAN: return "GQLA_ERR_BAD_SPLIT_PLAN: split_tokens must be a positive multiple of block_size and total_splits >= batch";
     case GQLA_ERR_HIP: return "GQLA_ERR_HIP: kernel launch failed";
+    case GQLA_ERR_SCRATCH_LIMIT: return "GQLA_ERR_SCRATCH_LIMIT: the call needs more workspace than the library's fixed scratch array (GQLA_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown gqla status";
   }
 }
@@ -295,6 +332,29 @@ int gqla_decode_mqa_absorb(const gqla_dims* d, int32_t batch, const void* q_nope
   hipError_t e = gqla::absorb_dispatch(d->num_heads / d->num_groups, d->s_q, d->d_latent,
                                        d->d_nope, d->d_v, d->d_rope, p, (hipStream_t)stream, &ok, false);
   return finish(e, ok);
+}
+
+int gqla_decode_mqa_absorb_noalloc(const gqla_dims* d, int32_t batch, const void* q_nope,
+                                   const void* q_rope, const void* latent_pages,
+                                   const int32_t* block_table, int32_t max_blocks,
+                                   const int32_t* cache_seqlens, const void* w_uk, const void* w_uv,
+                                   const int32_t* split_offsets, int32_t split_tokens,
+                                   int32_t total_splits, void* out, float* lse, void* stream) {
+  int st = check_decode(d, batch, q_nope, q_rope, latent_pages, block_table, max_blocks,
+                        cache_seqlens, split_offsets, split_tokens, total_splits, out, lse,
+                        nullptr, nullptr, false);
+  if (st != GQLA_OK) return st;
+  if (!w_uk || !w_uv) return GQLA_ERR_INVALID_ARG;
+  if (!aligned16(w_uk) || !aligned16(w_uv)) return GQLA_ERR_MISALIGNED;
+  if (batch == 0) return GQLA_OK;
+  const uint64_t need = gqla_mqa_absorb_workspace_bytes(d, batch, split_offsets ? total_splits : 0);
+  if (need == 0) return GQLA_ERR_INVALID_ARG;
+  if (need > GQLA_NOALLOC_SCRATCH_BYTES) return GQLA_ERR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  if (scratch_of_current_device((hipStream_t)stream, &ws) != hipSuccess) return GQLA_ERR_HIP;
+  return gqla_decode_mqa_absorb(d, batch, q_nope, q_rope, latent_pages, block_table, max_blocks,
+                                cache_seqlens, w_uk, w_uv, split_offsets, split_tokens, total_splits, out,
+                                lse, ws, need, stream);
 }
 
 uint64_t gqla_mqa_absorb_merge_workspace_bytes(const gqla_dims* d) {

@@ -72,6 +72,7 @@ extern "C" {
 #define GQLA_ERR_MISALIGNED (-3)
 #define GQLA_ERR_BAD_SPLIT_PLAN (-4)
 #define GQLA_ERR_HIP (-5)
+#define GQLA_ERR_SCRATCH_LIMIT (-6)
 
 /* Problem dimensions, in the pages' notation (paperlayer.ai section 3
  * "Architecture": h_q heads, g groups of per-head dim d_h, latent c^KV_t,
@@ -188,6 +189,28 @@ uint64_t gqla_mqa_absorb_workspace_bytes(const gqla_dims* d, int32_t batch, int3
  * answers 0 for, or offsets == NULL. */
 int gqla_mqa_absorb_workspace_offsets(const gqla_dims* d, int32_t batch, int32_t total_splits,
                                       uint64_t* offsets);
+
+/* gqla_decode_mqa_absorb without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, checks and results as
+ * gqla_decode_mqa_absorb; the workspace is a device array of
+ * GQLA_NOALLOC_SCRATCH_BYTES bytes compiled into the library, one per GPU,
+ * resolved on the first call on that GPU (the current device, which must be
+ * the stream's device) and held until the process ends.  The call allocates
+ * nothing.  A call whose workspace would exceed the array
+ * (gqla_mqa_absorb_workspace_bytes(d, batch, split_offsets ? total_splits : 0)
+ * > GQLA_NOALLOC_SCRATCH_BYTES) returns GQLA_ERR_SCRATCH_LIMIT before any HIP
+ * call.  Every call on one GPU uses the same array: calls that may overlap on
+ * one GPU (concurrent streams or threads) race and must be serialised by the
+ * caller.  The kernels write every scratch byte they later read, so nothing
+ * is cleared between calls. */
+#define GQLA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int gqla_decode_mqa_absorb_noalloc(const gqla_dims* d, int32_t batch, const void* q_nope,
+                                   const void* q_rope, const void* latent_pages,
+                                   const int32_t* block_table, int32_t max_blocks,
+                                   const int32_t* cache_seqlens, const void* w_uk, const void* w_uv,
+                                   const int32_t* split_offsets, int32_t split_tokens,
+                                   int32_t total_splits, void* out, float* lse, void* stream);
 
 /* Merge of MQA-absorb split partials in the latent space, then the
  * up-projection (paperlayer.ai section 4, "MQA-absorb path": attention runs

@@ -246,3 +246,19 @@ def test_absorb_merge_rejects_bad_arguments_on_the_host(lib):
     bad = dsv3(d_v=96)
     assert merge(lib, bad) == UNSUPPORTED
     assert merge(lib, d, batch=0) == OK               # nothing to do, nothing enqueued
+
+
+def test_noalloc_absorb_checks_arguments_and_its_scratch_limit_on_the_host(lib):
+    d = dsv3()
+    call = lambda **kw: lib.gqla_decode_mqa_absorb_noalloc(
+        ctypes.byref(d), kw.get("batch", 1), kw.get("q", A), A, A, A, 4, A, kw.get("wuk", A), A,
+        kw.get("split", None), kw.get("split_tokens", 0), kw.get("total", 0), kw.get("out", A), None, None)
+    assert call(q=None) == INVALID
+    assert call(wuk=None) == INVALID
+    assert call(q=ODD) == MISALIGNED
+    assert call(split=A, split_tokens=1000, total=4) == BADSPLIT
+    assert call(batch=0) == OK
+    # 64 x 4096 tokens in 64-token splits: the workspace exceeds the fixed 32 MiB scratch,
+    # rejected before any HIP call
+    assert call(batch=64, split=A, split_tokens=64, total=64 * 64) == -6
+    assert b"SCRATCH_LIMIT" in lib.gqla_status_string(-6)
