@@ -466,19 +466,22 @@ def main():
         for _, fn in paths:
             fn()
     torch.cuda.synchronize()
-    # timed region: K steps; per-path events on the launch stream
+    # timed region: K steps, one event on the launch stream between consecutive calls (a call's
+    # time is the interval between the events around it; each event adds a marker packet between
+    # two calls, so one per call rather than a pair)
     evs = {name: [] for name, _ in paths}
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t_start.record()
+    marks = [torch.cuda.Event(enable_timing=True)]
+    marks[0].record()
+    t_start = marks[0]
     for _ in range(args.steps):
         for name, fn in paths:
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
             fn()
-            b.record()
-            evs[name].append((a, b))
-    t_end.record()
+            e = torch.cuda.Event(enable_timing=True)
+            e.record()
+            evs[name].append((marks[-1], e))
+            marks.append(e)
+    t_end = marks[-1]
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / args.steps
