@@ -58,8 +58,6 @@ __device__ __forceinline__ void dma16_free(const void* base, uint32_t voff_bytes
                :: "v"(voff_bytes), "s"(base), "s"(m0v) : "m0");
 }
 
-__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
-
 template <int HPG, int SQ, int R, int DR, int QC>
 struct WideCfg {
   static constexpr int BS = 64;

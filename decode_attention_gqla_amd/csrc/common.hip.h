@@ -165,6 +165,9 @@ __device__ __forceinline__ int sload_i32(const int32_t* ptr) {
   return v;
 }
 
+// Scheduling fence: the compiler moves no instruction across it.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
 // Workgroup barrier for LDS hand-offs: this wave's LDS reads and writes are
 // complete before it arrives.
 __device__ __forceinline__ void block_sync_lds() {
