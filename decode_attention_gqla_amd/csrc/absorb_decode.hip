@@ -141,10 +141,10 @@ void absorb_decode_narrow_kernel(DecodeParams p) {
   const int c = lane & 15, qq = lane >> 4;        // 16x16 MFMA lane coordinates
   int b, lo, hi;
   if (p.split_offsets) {
-    b = split_owner(p.split_offsets, p.batch, u);
-    const int j = u - p.split_offsets[b];
-    lo = j * p.split_tokens;
-    hi = min(lo + p.split_tokens, p.seqlens[b]);
+    const UnitOwner own = unit_owner(p.split_offsets, p.seqlens, p.batch, u);
+    b = own.b;
+    lo = (u - own.first) * p.split_tokens;         // a multiple of BS
+    hi = min(lo + p.split_tokens, own.len);
   } else {
     b = u;
     lo = 0;

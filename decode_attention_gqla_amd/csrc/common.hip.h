@@ -187,14 +187,35 @@ __device__ __forceinline__ void block_sync_lds() {
 // chunk offsets.
 __device__ __forceinline__ int tile_swz(int t) { return 4 * ((t >> 1) & 1) + 2 * ((t >> 2) & 1); }
 
-// Find the sequence owning split w: largest b with split_offsets[b] <= w.
-__device__ __forceinline__ int split_owner(const int32_t* __restrict__ offs, int batch, int w) {
-  int lo = 0, hi = batch - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (offs[mid] <= w) lo = mid; else hi = mid - 1;
+// The sequence that owns unit u under a split plan: the last b with
+// offs[b] <= u (the offsets are nondecreasing prefix sums from offs[0] = 0),
+// its first unit offs[b] and its length lens[b].  One load per lane and 64
+// sequences (lane j reads offs[j] and lens[j]; the owner's values come from
+// its lane), rather than a chain of dependent loads.  u must be wave-uniform
+// and below offs[batch]; every lane of the wave must be active.
+struct UnitOwner {
+  int b, first, len;
+};
+__device__ __forceinline__ UnitOwner unit_owner(const int32_t* __restrict__ offs, const int32_t* __restrict__ lens,
+                                                int batch, int u) {
+  const int lane = (int)(threadIdx.x & 63);
+  UnitOwner r = {0, 0, 0};
+  int cnt = 0;
+  for (int c0 = 0; c0 < batch; c0 += 64) {
+    const int j = c0 + lane;
+    const bool in = j < batch;
+    const int oj = in ? offs[j] : 0x7fffffff;
+    const int lj = in ? lens[j] : 0;
+    const int nb = __builtin_popcountll(__builtin_amdgcn_ballot_w64(oj <= u));
+    if (nb > 0) {                                 // the last candidate so far is lane nb - 1
+      r.first = __builtin_amdgcn_readlane(oj, nb - 1);
+      r.len = __builtin_amdgcn_readlane(lj, nb - 1);
+    }
+    cnt += nb;
+    if (nb < 64) break;                           // the prefix ends in this chunk
   }
-  return lo;
+  r.b = cnt - 1;
+  return r;
 }
 
 }  // namespace gqla

@@ -156,7 +156,7 @@ __global__ __launch_bounds__(256) void gqa_decode_kernel(DecodeParams p) {
   const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);   // this wave's 16-row tile
   if constexpr (SPARSE) {                         // units: (sequence, entry range) x group
     if (p.split_offsets) {
-      b = split_owner(p.split_offsets, p.batch, u);
+      b = unit_owner(p.split_offsets, p.seqlens, p.batch, u).b;
       lo = (u - p.split_offsets[b]) * p.split_tokens;
       hi = min(lo + p.split_tokens, p.topk_pad);
     } else {
@@ -166,10 +166,10 @@ __global__ __launch_bounds__(256) void gqa_decode_kernel(DecodeParams p) {
     }
     if (p.seqlens[b] <= 0) hi = lo;               // no entry is visible in an empty sequence
   } else if (p.split_offsets) {
-    b = split_owner(p.split_offsets, p.batch, u);
-    const int j = u - p.split_offsets[b];
-    lo = j * p.split_tokens;
-    hi = min(lo + p.split_tokens, p.seqlens[b]);
+    const UnitOwner own = unit_owner(p.split_offsets, p.seqlens, p.batch, u);
+    b = own.b;
+    lo = (u - own.first) * p.split_tokens;
+    hi = min(lo + p.split_tokens, own.len);
   } else {
     b = u;
     lo = 0;
