@@ -14,6 +14,8 @@
 // latent rows come straight from HBM as 16-byte operand loads.  Both K and V
 // are produced transposed, K^T = W_UK^T C^T and V^T = W_UV^T C^T, so every
 // lane writes 4 consecutive dims of one token (both blocks token-major).
+#include <type_traits>
+
 #include "common.hip.h"
 #include "params.hip.h"
 
@@ -142,6 +144,255 @@ __device__ __forceinline__ void expand_body(const ExpandParams& p, int64_t tile,
   }
 }
 
+// ---------------------------------------------------------------------------
+// The 512 + 64 latent row with d_nope = d_v = 128: one workgroup of four waves
+// (one per SIMD, 512 registers each) per 4 pages; wave w owns page 4 wg + w
+// (64 tokens) for every (group, K or V) block.
+//   * The page's latent rows stay in accumulation registers for the whole
+//     workgroup as the B operands of K^T = W^T C^T (lane (q, c) holds
+//     C[token 16 nt + c][32 kc + 8 q .. +7]: 4 token tiles x 16 k chunks,
+//     256 registers), read from HBM once instead of once per block.
+//   * Each block W[G] (512 x 128 bf16, shared by every workgroup from L2) is
+//     taken in two 64-dim halves; a phase covers one half over 256 k rows, a
+//     32 KB slice copied into LDS by direct copy (global_load_lds_dwordx4):
+//     four slice buffers, three slices in flight, one workgroup barrier per
+//     phase.  The A operand (8 consecutive k of one output dim per lane) is a
+//     transposing read (ds_read_b64_tr_b16) of the slice's 128-byte rows;
+//     16-byte chunk x of row r sits at x ^ s(r),
+//     s(r) = 2 (((r >> 1) & 1) + 2 ((r >> 3) & 1)), which puts each 32-lane
+//     pass of the read on 64 distinct banks (checked exhaustively against the
+//     measured pass structure).  Each A operand feeds four MFMAs (the four
+//     token tiles).
+//   * The same MFMA (16x16x32) over the same 32-wide k chunks in the same
+//     order as gqla_append_tokens, so both write bit-identical K and V.
+//   * A finished half-block (64 tokens x 64 dims) is rounded to bf16 and
+//     staged in LDS (the wave's 8 KB, token rows of 128 bytes, chunk x of
+//     token t at x ^ ((t >> 1) & 7): conflict-free writes and reads), then
+//     stored during the next two phases with one store instruction per 8
+//     whole rows (full 128-byte lines), so that the output writes of all
+//     workgroups (which run in step) spread over the run instead of meeting
+//     in one burst per block.
+//   * The copy and store instructions of a phase sit between its MFMAs (one
+//     every four), where their issue overlaps the matrix work.
+template <int R, int DH, int DR>
+struct ExpandPagesCfg {
+  static constexpr int BS = 64;
+  static constexpr int ROW = R + DR;
+  static constexpr int NW = 4;                     // waves = pages per workgroup
+  static constexpr int DHH = 64;                   // output dims per pass (half a block)
+  static constexpr int NH = DH / DHH;              // passes per block
+  static constexpr int KH = 256;                   // weight rows per phase
+  static constexpr int NKH = R / KH;               // phases per pass
+  static constexpr int SBYTES = KH * DHH * 2;      // one slice in LDS
+  static constexpr int NBUF = 4;
+  static constexpr int NI = SBYTES / 1024;         // copy instructions per slice
+  static constexpr int NIW = NI / NW;              // per wave
+  static constexpr int KC = R / 32;                // k chunks of the product
+  static constexpr int KCP = KH / 32;              // per phase
+  static constexpr int MT = DHH / 16;              // 16-dim output tiles per pass
+  static constexpr int NT = BS / 16;               // 16-token tiles of a page
+  static constexpr int NPART = 2;                  // store parts of a finished pass
+  static constexpr int STAGE = BS * DHH * 2;       // a wave's staged pass (bytes)
+  static constexpr int NSI = STAGE / 1024;         // its store instructions (8 token rows each)
+  static constexpr int NSP = NSI / NPART;          // per part
+  static constexpr int OFF_STAGE = NBUF * SBYTES;
+  static constexpr int LDS_BYTES = OFF_STAGE + NW * STAGE;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(DHH == 64 && DH % DHH == 0, "128-byte slice rows: the chunk swizzle covers 8 chunks");
+  static_assert(R % KH == 0 && NI % NW == 0 && KH * DH * 2 <= 65536, "slice tiling, 16-bit copy offsets");
+  static_assert(NKH >= NPART && NSI % NPART == 0, "a pass's stores fit in the next pass's phases");
+};
+
+__device__ __forceinline__ int ex_swz(int r) { return 2 * (((r >> 1) & 1) + 2 * ((r >> 3) & 1)); }
+
+template <int R, int DH, int DR>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void expand_pages_kernel(ExpandParams p) {
+  using C = ExpandPagesCfg<R, DH, DR>;
+  constexpr int BS = C::BS, ROW = C::ROW, NW = C::NW, NIW = C::NIW, KCP = C::KCP, NKH = C::NKH, NH = C::NH;
+  constexpr int MT = C::MT, NT = C::NT, KC = C::KC, DHH = C::DHH, NPART = C::NPART, NSP = C::NSP;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[C::LDS_BYTES];
+  lds_u8_t* const lds = (lds_u8_t*)lds_raw;
+  const int g = p.num_groups;
+  const int npass = 2 * g * NH;                    // (group, K or V, half) passes
+  const int nph = npass * NKH;                     // phases
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane & 15, q = lane >> 4;
+  const int64_t idx = (int64_t)blockIdx.x * NW + w;
+  const bool active = idx < p.n_expand;            // inactive waves compute on page 0 and store nothing
+  const int64_t pidx = active ? idx : 0;
+  const int64_t page = p.page_ids ? (int64_t)p.page_ids[pidx] : pidx;
+  const uint16_t* lat = p.latent + (size_t)page * BS * ROW;
+  const size_t page_elems = (size_t)BS * (g * 2 * DH + DR);
+  uint16_t* dst = p.expanded + (size_t)page * page_elems;
+
+  // Phase pi: pass ps = pi / NKH (block blk = ps / NH, half h = ps % NH),
+  // weight rows KH (pi % NKH) .. +KH-1, dims DHH h .. +DHH-1.
+  // This wave's copy instructions of every slice: instruction k (of the
+  // slice's NI) fills LDS bytes 1024 k ..; position P = 64 k + lane holds
+  // row P / 8, physical chunk P % 8 = logical chunk (P % 8) ^ s(row).
+  // Source offsets (bytes from the slice's first row and dim) packed two per
+  // register.
+  uint32_t cpo[(NIW + 1) / 2];
+#pragma unroll
+  for (int kk = 0; kk < NIW; ++kk) {
+    const int P = (w * NIW + kk) * 64 + lane;
+    const int r = P / 8, pc = P % 8;
+    const uint32_t off = (uint32_t)(r * DH * 2 + ((pc ^ ex_swz(r)) * 16));
+    if (kk % 2 == 0) cpo[kk / 2] = off; else cpo[kk / 2] |= off << 16;
+  }
+  auto slice_src = [&](int pi) -> const uint16_t* {
+    const int ps = pi / NKH, blk = ps / NH, h = ps % NH, kh = pi % NKH;
+    const uint16_t* W = ((blk & 1) ? p.w_uv : p.w_uk) + (size_t)(blk >> 1) * R * DH;
+    return W + (size_t)kh * C::KH * DH + h * DHH;
+  };
+  auto copy_part = [&](const uint16_t* src, int pi, int kk) {   // copy instruction kk of slice pi
+    const uint32_t off = (kk % 2 == 0) ? (cpo[kk / 2] & 0xffffu) : (cpo[kk / 2] >> 16);
+    dma16(src, off, lds + (pi % C::NBUF) * C::SBYTES + (w * NIW + kk) * 1024);
+  };
+  auto copy_slice = [&](int pi) {
+    const uint16_t* src = slice_src(pi);
+#pragma unroll
+    for (int kk = 0; kk < NIW; ++kk) copy_part(src, pi, kk);
+  };
+
+  // ---- start: the page's latent rows into accumulation registers; slices
+  // 0, 1, 2 ----
+  bf16x8 cb[NT][KC];
+  {
+    const uint16_t* crow = lat + (size_t)c * ROW + 8 * q;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) cb[nt][kc] = ld_bf16x8(crow + (size_t)16 * nt * ROW + 32 * kc);
+  }
+#pragma unroll
+  for (int j = 0; j < 3; ++j)
+    if (j < nph) copy_slice(j);
+  vm_wait<0>();
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) asm volatile("" : "+a"(cb[nt][kc]));
+  block_sync_lds();
+
+  // transposing-read bases of output tile mt: row 8 q + (c >> 2) of the
+  // k chunk, dims 16 mt + 4 (c & 3) .. +3 of the half; + (32 kc + 4 rd) rows
+  int ab[MT];
+  {
+    const int r0 = 8 * q + (c >> 2);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      ab[mt] = r0 * DHH * 2 + (((2 * mt + ((c & 3) >> 1)) ^ ex_swz(r0)) * 16) + 8 * (c & 1);
+  }
+  auto a_operand = [&](const lds_u8_t* buf, int kc, int mt) -> bf16x8 {
+    const int imm = 32 * kc * DHH * 2;
+    const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(buf + ab[mt] + imm));
+    const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(buf + ab[mt] + imm + 4 * DHH * 2));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  f32x4 acc[MT][NT];
+  lds_u8_t* const stage = lds + C::OFF_STAGE + w * C::STAGE;
+  // staged byte offset of 16-byte chunk x of token t
+  auto stage_off = [&](int t, int x) -> int { return t * DHH * 2 + ((x ^ ((t >> 1) & 7)) * 16); };
+  // the output rows of pass ps (token-major, DH elements apart)
+  auto pass_dst = [&](int ps) -> uint16_t* {
+    const int blk = ps / NH, h = ps % NH;
+    return dst + (size_t)(blk >> 1) * BS * 2 * DH + (blk & 1) * BS * DH + h * DHH;
+  };
+  // store instruction i of a staged pass: tokens 8 i .. 8 i + 7, lane l writes
+  // chunk l % 8 of token 8 i + l / 8
+  auto staged = [&](int i) -> u32x4 {
+    return *(const lds_u32x4_t*)(stage + stage_off(8 * i + lane / 8, lane % 8));
+  };
+  auto store_row8 = [&](uint16_t* ob, int i, const u32x4& v) {
+    *reinterpret_cast<u32x4*>(ob + (size_t)(8 * i + lane / 8) * DH + 8 * (lane % 8)) = v;
+  };
+  // Phase pi (k step kh of pass ps): the MFMAs of slice pi, with the copies
+  // of slice pi + 3 (cpy; its buffer was last read in phase pi - 1) and part
+  // kh of the previous pass's stores (st) between them; after the pass's last
+  // phase the pass is staged.  FIRST: the pass's first phase (its first k
+  // chunk starts the accumulators from zero).
+  auto mfmas = [&](int pi, auto first, bool cpy, bool st) {
+    constexpr bool FIRST = decltype(first)::value;
+    const int kh = pi % NKH;
+    const lds_u8_t* buf = lds + (pi % C::NBUF) * C::SBYTES;
+    const uint16_t* csrc = slice_src(pi + 3);
+    uint16_t* ob = pass_dst(pi / NKH - 1);
+    u32x4 sv[NSP];
+    if (st) {
+#pragma unroll
+      for (int i = 0; i < NSP; ++i) sv[i] = staged(kh * NSP + i);
+    }
+    constexpr int NS = KCP * MT;                   // A operands
+    constexpr int PD = 2;
+    static_assert(NS >= 4 * NIW && NS >= 4 * NSP, "copy and store slots");
+    bf16x8 a[PD + 1];
+#pragma unroll
+    for (int j = 0; j < PD; ++j) a[j] = a_operand(buf, j / MT, j % MT);
+    sched_fence();
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const int kc = j / MT, mt = j % MT;
+      if (j + PD < NS) a[(j + PD) % (PD + 1)] = a_operand(buf, (j + PD) / MT, (j + PD) % MT);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const bf16x8 bq = cb[nt][KCP * kh + kc];
+        acc[mt][nt] = mfma16(a[j % (PD + 1)], bq, (FIRST && kc == 0) ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[mt][nt]);
+      }
+      if (j % 4 == 0 && j / 4 < NIW && cpy) copy_part(csrc, pi + 3, j / 4);
+      if (j % 4 == 2 && j / 4 < NSP && st) store_row8(ob, kh * NSP + j / 4, sv[j / 4]);
+      sched_fence();
+    }
+  };
+  auto stage_pass = [&]() {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int t = 16 * nt + c, d = 16 * mt + 4 * q;     // 4 dims of token t
+        const u32x2 pk = {pack_bf16x2(acc[mt][nt][0], acc[mt][nt][1]), pack_bf16x2(acc[mt][nt][2], acc[mt][nt][3])};
+        *(__attribute__((address_space(3))) u32x2*)(stage + stage_off(t, d / 8) + (d % 8) * 2) = pk;
+      }
+  };
+  // Phase pi, then slice pi + 1 landed (barrier).  The wait counts only the
+  // copies issued after slice pi + 1's; stores among them at worst make it
+  // wait longer.  Every wave reads only its own staged rows.
+  auto phase = [&](int pi, auto first) {
+    const int ps = pi / NKH, kh = pi % NKH;
+    mfmas(pi, first, pi + 3 < nph, active && ps > 0 && kh < NPART);
+    if (kh == NKH - 1) stage_pass();
+    if (pi + 3 < nph) vm_wait<2 * NIW>();
+    else if (pi + 2 < nph) vm_wait<NIW>();
+    else vm_wait<0>();
+    block_sync_lds();
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  for (int ps = 0; ps < npass; ++ps) {
+    phase(ps * NKH, T{});
+#pragma unroll
+    for (int kh = 1; kh < NKH; ++kh) phase(ps * NKH + kh, F{});
+  }
+  if (active) {                                    // the last pass
+    uint16_t* ob = pass_dst(npass - 1);
+#pragma unroll
+    for (int i = 0; i < C::NSI; ++i) store_row8(ob, i, staged(i));
+  }
+
+  // the shared rope key, copied unchanged
+  if (active) {
+    uint16_t* rope = dst + (size_t)g * BS * 2 * DH;
+    for (int id = lane; id < BS * DR / 8; id += 64) {
+      const int slot = id / (DR / 8), part = id % (DR / 8);
+      *reinterpret_cast<u32x4*>(rope + slot * DR + part * 8) =
+          *reinterpret_cast<const u32x4*>(lat + (size_t)slot * ROW + R + part * 8);
+    }
+  }
+}
+
 hipError_t expand_dispatch(int r, int dn, int dv, int dr, const ExpandParams& p, hipStream_t stream,
                            bool* supported) {
   *supported = true;
@@ -152,7 +403,10 @@ hipError_t expand_dispatch(int r, int dn, int dv, int dr, const ExpandParams& p,
   if (grid64 > 0x7fffffff) { *supported = false; return hipSuccess; }
   const unsigned grid = (unsigned)grid64;
   if (r == 512 && dn == 128 && dv == 128 && dr == 64) {
-    hipLaunchKernelGGL((expand_kernel<512, 128, 64>), dim3(grid), dim3(256), 0, stream, p);
+    using C = ExpandPagesCfg<512, 128, 64>;
+    const int64_t nwg = (p.n_expand + C::NW - 1) / C::NW;
+    if (nwg > 0x7fffffff) { *supported = false; return hipSuccess; }
+    hipLaunchKernelGGL((expand_pages_kernel<512, 128, 64>), dim3((unsigned)nwg), dim3(64 * C::NW), 0, stream, p);
   } else if (r == 64 && dn == 32 && dv == 32 && dr == 16) {
     hipLaunchKernelGGL((expand_kernel<64, 32, 16>), dim3(grid), dim3(256), 0, stream, p);
   } else {
