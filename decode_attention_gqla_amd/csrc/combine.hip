@@ -9,7 +9,11 @@
 //
 // One thread per 4 consecutive output dims of one (sequence, row); a row of
 // d_v dims is d_v/4 adjacent threads, so every split partial row is read with
-// fully coalesced 16-byte loads.
+// fully coalesced 16-byte loads.  The lse values and partial rows of up to SC
+// splits are loaded together (one memory latency per batch of splits, not one
+// per split); a later batch with a larger maximum rescales what is summed.
+// With at most SC splits the sums are formed in split order exactly as in
+// the formula above.
 #include "common.hip.h"
 #include "params.hip.h"
 
@@ -18,6 +22,7 @@ namespace gqla {
 template <int DV>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   constexpr int TPR = DV / 4;                      // threads per row
+  constexpr int SC = 8;                            // splits per load batch
   const int tid = blockIdx.x * 256 + threadIdx.x;
   const int gr = tid / TPR;                         // global row = b * rows + r
   const int part = tid % TPR;
@@ -25,17 +30,34 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   const int b = gr / p.rows, r = gr % p.rows;
   const int s0 = p.split_offsets[b], s1 = p.split_offsets[b + 1];
 
-  float m = -INFINITY;
-  for (int s = s0; s < s1; ++s) m = fmaxf(m, p.part_lse[(size_t)s * p.rows + r]);
+  float m = -INFINITY, z = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float z = 0.f;
-  if (m != -INFINITY) {
-    for (int s = s0; s < s1; ++s) {
-      const float ls = p.part_lse[(size_t)s * p.rows + r];
-      if (ls == -INFINITY) continue;
-      const float w = expf(ls - m);
-      const f32x4 v = *reinterpret_cast<const f32x4*>(p.part_out + ((size_t)s * p.rows + r) * DV + 4 * part);
-      acc += w * v;
+  for (int sb = s0; sb < s1; sb += SC) {
+    float ls[SC];
+    f32x4 v[SC];
+#pragma unroll
+    for (int k = 0; k < SC; ++k) {
+      const bool have = sb + k < s1;
+      const size_t row = (size_t)(have ? sb + k : s0) * p.rows + r;
+      ls[k] = have ? p.part_lse[row] : -INFINITY;
+      v[k] = have ? *reinterpret_cast<const f32x4*>(p.part_out + row * DV + 4 * part) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float bm = ls[0];
+#pragma unroll
+    for (int k = 1; k < SC; ++k) bm = fmaxf(bm, ls[k]);
+    const float mn = fmaxf(m, bm);
+    if (mn == -INFINITY) continue;                  // no visible token so far
+    if (m != -INFINITY && m != mn) {
+      const float sc = expf(m - mn);
+      acc *= sc;
+      z *= sc;
+    }
+    m = mn;
+#pragma unroll
+    for (int k = 0; k < SC; ++k) {
+      if (ls[k] == -INFINITY) continue;             // empty split (its partial row may hold anything)
+      const float w = expf(ls[k] - m);
+      acc += w * v[k];
       z += w;
     }
   }
