@@ -54,8 +54,10 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the steps take about 0.3 ms each: 200 warmup steps bring the GPU to its steady state (with 5,
+    # the timed steps ran 15% slower)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--absorb-split", type=int, default=2048,
                     help="tokens per split-KV partition of the absorb path (0 = no split)")
     ap.add_argument("--gqa-split", type=int, default=0,
@@ -466,14 +468,25 @@ def main():
         for _, fn in paths:
             fn()
     torch.cuda.synchronize()
-    # timed region: K steps, one event on the launch stream between consecutive calls (a call's
-    # time is the interval between the events around it; each event adds a marker packet between
-    # two calls, so one per call rather than a pair)
-    evs = {name: [] for name, _ in paths}
+    # timed region: K steps between two events on the launch stream, nothing in between (a
+    # timing event between calls adds a marker packet that the queue waits on: about 3 us per
+    # marker measured on this step)
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    t_start.record()
+    for _ in range(args.steps):
+        for name, fn in paths:
+            fn()
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    # per-path breakdown: the same K steps again, one event between consecutive calls (a call's
+    # time is the interval between the events around it, so it includes one marker: these
+    # per-path times, and the fractions of the roofline computed from them, are upper bounds)
+    evs = {name: [] for name, _ in paths}
     marks = [torch.cuda.Event(enable_timing=True)]
     marks[0].record()
-    t_start = marks[0]
     for _ in range(args.steps):
         for name, fn in paths:
             fn()
@@ -481,10 +494,8 @@ def main():
             e.record()
             evs[name].append((marks[-1], e))
             marks.append(e)
-    t_end = marks[-1]
     torch.cuda.synchronize()
-    ms_total = t_start.elapsed_time(t_end)
-    ms_step = ms_total / args.steps
+    ms_step_marked = marks[0].elapsed_time(marks[-1]) / args.steps
     per_path = {}
     for name, _ in paths:
         us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs[name])
@@ -579,6 +590,7 @@ def main():
         "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "ms_per_step_with_call_markers": ms_step_marked,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": WORKLOAD, "global_batch": B, "seq_len": 4096,
