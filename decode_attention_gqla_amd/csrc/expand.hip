@@ -14,6 +14,8 @@
 // latent rows come straight from HBM as 16-byte operand loads.  Both K and V
 // are produced transposed, K^T = W_UK^T C^T and V^T = W_UV^T C^T, so every
 // lane writes 4 consecutive dims of one token (both blocks token-major).
+#include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "common.hip.h"
@@ -215,11 +217,26 @@ void expand_pages_kernel(ExpandParams p) {
   lds_u8_t* const lds = (lds_u8_t*)lds_raw;
   const int g = p.num_groups;
   const int npass = 2 * g * NH;                    // (group, K or V, half) passes
-  const int nph = npass * NKH;                     // phases
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, q = lane >> 4;
-  const int64_t idx = (int64_t)blockIdx.x * NW + w;
+  // This workgroup's segment: page quad `quad` (wave w: page 4 quad + w),
+  // passes ps0 .. ps1 - 1.  The first whole_quads workgroups take a quad
+  // whole; each later one takes one of `pieces` pass ranges of a quad, so the
+  // last, partial round of quads is spread over many CUs.
+  const int64_t wi = blockIdx.x;
+  int64_t quad = wi;
+  int ps0 = 0, ps1 = npass;
+  if (wi >= p.whole_quads) {
+    const int r = (int)(wi - p.whole_quads);     // below CUs * passes: 32-bit division
+    const int j = r % p.pieces;
+    quad = p.whole_quads + r / p.pieces;
+    ps0 = j * npass / p.pieces;
+    ps1 = (j + 1) * npass / p.pieces;
+  }
+  __builtin_assume(ps0 >= 0);                      // (so the k step of a phase, pi % NKH, is known)
+  const int nph = ps1 * NKH;                       // end of the segment's phases
+  const int64_t idx = quad * NW + w;
   const bool active = idx < p.n_expand;            // inactive waves compute on page 0 and store nothing
   const int64_t pidx = active ? idx : 0;
   const int64_t page = p.page_ids ? (int64_t)p.page_ids[pidx] : pidx;
@@ -269,7 +286,7 @@ void expand_pages_kernel(ExpandParams p) {
   }
 #pragma unroll
   for (int j = 0; j < 3; ++j)
-    if (j < nph) copy_slice(j);
+    if (ps0 * NKH + j < nph) copy_slice(ps0 * NKH + j);
   vm_wait<0>();
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
@@ -371,7 +388,7 @@ void expand_pages_kernel(ExpandParams p) {
   // wait longer.  Every wave reads only its own staged rows.
   auto phase = [&](int pi, auto first) {
     const int ps = pi / NKH, kh = pi % NKH;
-    mfmas(pi, first, pi + 3 < nph, active && ps > 0 && kh < NPART);
+    mfmas(pi, first, pi + 3 < nph, active && ps > ps0 && kh < NPART);
     if (kh == NKH - 1) stage_pass();
     if (pi + 3 < nph) vm_wait<2 * NIW>();
     else if (pi + 2 < nph) vm_wait<NIW>();
@@ -380,19 +397,19 @@ void expand_pages_kernel(ExpandParams p) {
   };
   using T = std::true_type;
   using F = std::false_type;
-  for (int ps = 0; ps < npass; ++ps) {
+  for (int ps = ps0; ps < ps1; ++ps) {
     phase(ps * NKH, T{});
 #pragma unroll
     for (int kh = 1; kh < NKH; ++kh) phase(ps * NKH + kh, F{});
   }
-  if (active) {                                    // the last pass
-    uint16_t* ob = pass_dst(npass - 1);
+  if (active) {                                    // the segment's last pass
+    uint16_t* ob = pass_dst(ps1 - 1);
 #pragma unroll
     for (int i = 0; i < C::NSI; ++i) store_row8(ob, i, staged(i));
   }
 
-  // the shared rope key, copied unchanged
-  if (active) {
+  // the shared rope key, copied unchanged (by the segment that starts the page)
+  if (active && ps0 == 0) {
     uint16_t* rope = dst + (size_t)g * BS * 2 * DH;
     for (int id = lane; id < BS * DR / 8; id += 64) {
       const int slot = id / (DR / 8), part = id % (DR / 8);
@@ -400,6 +417,25 @@ void expand_pages_kernel(ExpandParams p) {
           *reinterpret_cast<const u32x4*>(lat + (size_t)slot * ROW + R + part * 8);
     }
   }
+}
+
+// Compute units of the current device, looked up once per device.
+hipError_t cu_count(int* n) {
+  static std::mutex mu;
+  static int cached[64] = {0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cached[dev] == 0) {
+    int v = 0;
+    e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    cached[dev] = v > 0 ? v : 1;
+  }
+  *n = cached[dev];
+  return hipSuccess;
 }
 
 hipError_t expand_dispatch(int r, int dn, int dv, int dr, const ExpandParams& p, hipStream_t stream,
@@ -413,9 +449,23 @@ hipError_t expand_dispatch(int r, int dn, int dv, int dr, const ExpandParams& p,
   const unsigned grid = (unsigned)grid64;
   if (r == 512 && dn == 128 && dv == 128 && dr == 64) {
     using C = ExpandPagesCfg<512, 128, 64>;
-    const int64_t nwg = (p.n_expand + C::NW - 1) / C::NW;
+    // One workgroup per CU at a time (it takes all of a CU's LDS).  The quads
+    // of the last, partial round (quads mod CUs) are each cut into up to
+    // CUs / leftover pass ranges, so that round takes about one pass instead
+    // of a whole quad on a few CUs.
+    int cus = 0;
+    const hipError_t e = cu_count(&cus);
+    if (e != hipSuccess) return e;
+    const int64_t quads = (p.n_expand + C::NW - 1) / C::NW;
+    const int64_t left = quads % cus;
+    const int npass = 2 * p.num_groups * C::NH;
+    const int pieces = left > 0 ? (int)std::min<int64_t>(npass, cus / left) : 1;
+    ExpandParams q = p;
+    q.whole_quads = quads - left;
+    q.pieces = pieces;
+    const int64_t nwg = q.whole_quads + left * pieces;
     if (nwg > 0x7fffffff) { *supported = false; return hipSuccess; }
-    hipLaunchKernelGGL((expand_pages_kernel<512, 128, 64>), dim3((unsigned)nwg), dim3(64 * C::NW), 0, stream, p);
+    hipLaunchKernelGGL((expand_pages_kernel<512, 128, 64>), dim3((unsigned)nwg), dim3(64 * C::NW), 0, stream, q);
   } else if (r == 64 && dn == 32 && dv == 32 && dr == 16) {
     hipLaunchKernelGGL((expand_kernel<64, 32, 16>), dim3(grid), dim3(256), 0, stream, p);
   } else {

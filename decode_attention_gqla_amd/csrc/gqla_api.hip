@@ -261,6 +261,8 @@ int gqla_expand_cache(const gqla_dims* d, const void* latent_pages, const void* 
   p.expanded = (uint16_t*)expanded_pages;
   p.n_expand = num_pages_to_expand;
   p.num_groups = d->num_groups;
+  p.whole_quads = 0;                               // (set by the launcher)
+  p.pieces = 1;
   bool ok = true;
   hipError_t e = gqla::expand_dispatch(d->d_latent, d->d_nope, d->d_v, d->d_rope, p,
                                        (hipStream_t)stream, &ok);

@@ -56,6 +56,10 @@ struct ExpandParams {
   uint16_t* expanded;            // [n_pages][page_elems]
   int64_t n_expand;              // pages to expand
   int32_t num_groups;
+  // expand_pages_kernel: workgroups [0, whole_quads) take page quads whole,
+  // the rest take one of `pieces` pass ranges of each following quad
+  int64_t whole_quads;
+  int32_t pieces;
 };
 
 struct AppendParams {

@@ -71,6 +71,35 @@ def test_expand_random_weights_within_one_bf16_ulp(name):
     assert np.array_equal(got[:, -d.bs * d.d_R:], ref[:, -d.bs * d.d_R:])
 
 
+def test_expand_full_pool_whole_quads_and_pieces_agree():
+    # 1025 pages: on a 256-CU GPU, 256 workgroups expand whole page quads and the
+    # leftover quad's passes are spread over 32 more; the same pages expanded by a
+    # call with a short page list (pass pieces only) must be identical bit for bit,
+    # and sampled pages (the last quad's included) meet the oracle's bound
+    log("expand/full pool (1025 pages)")
+    case = config_case("dsv3", 1, batch=16, ctx=4096)
+    d = dims_of(case)
+    gc = GpuCase(case)
+    n = case.pages.shape[0]
+    assert n == 1025
+    E = gc.expand()
+    ids = [0, 1, 511, 1021, 1022, 1023, 1024]
+    E_sub = torch.full_like(E, 3.0)
+    G.gqla_expand_cache(gc.d, gc.pages, gc.w_uk, gc.w_uv, E_sub,
+                        page_ids=torch.tensor(ids, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    for p in ids:
+        assert torch.equal(E_sub[p], E[p]), p
+    sample = [0, 511, 1023]                                  # 1024 is the spare (zero) page
+    ref = expand_pages(f64(case.pages), f64(case.w_uk), f64(case.w_uv), d, page_ids=sample)
+    mag = expand_pages(np.abs(f64(case.pages)), np.abs(f64(case.w_uk)), np.abs(f64(case.w_uv)), d,
+                       page_ids=sample)
+    got = f64(E)[sample]
+    bound = _expected_ulp_bound(ref) + d.r * 2.0 ** -24 * mag * 1.01
+    assert np.all(np.abs(got - ref) <= bound)
+    assert torch.all(E[1024] == 0)
+
+
 def test_expand_page_list_touches_only_listed_pages():
     log("expand/page_ids")
     case = config_case("tiny", 1, batch=2, ctx=256)
