@@ -196,25 +196,12 @@ def measure_g4(G, rf, config_case, steps: int, absorb_split: int):
         "gqa": lambda: G.gqla_decode_gqa(d, qn, qr, E, bt, sl, out=out, lse=lse, split_offsets=og,
                                          split_tokens=gsplit, total_splits=tg, part_out=po, part_lse=pl),
     }
-    for _ in range(3):
-        for fn in fns.values():
-            fn()
-    torch.cuda.synchronize()
-    evs = {k: [] for k in fns}
-    for _ in range(steps):
-        for k, fn in fns.items():
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            fn()
-            b.record()
-            evs[k].append((a, b))
-    torch.cuda.synchronize()
+    us_med = time_alternating(fns, steps)
     works = {"mqa_absorb": rf.work_absorb(lens, 128, 4, 512, 64, 128, 128, 1),
              "gqa": rf.work_gqa(lens, 128, 4, 64, 128, 128, 1)}
     res = {}
     for k in fns:
-        us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs[k])
-        med = us[len(us) // 2]
+        med = us_med[k]
         w = works[k]
         res[k] = {"us_median": med, "tok_s": B / (med * 1e-6), "roofline_us": w.roofline_us(),
                   "roofline_frac": w.roofline_us() / med, "bound": w.bound(), "alg_bytes": w.bytes}
@@ -226,26 +213,51 @@ def measure_g4(G, rf, config_case, steps: int, absorb_split: int):
 
 def time_alternating(fns: dict, steps: int) -> dict:
     """Median microseconds per call of each function, calling them in turn (each path's cache then
-    flushes the other's from the 256 MB memory-side cache, as in a step)."""
+    flushes the other's from the 256 MB memory-side cache, as in a step).  One HIP event between
+    consecutive calls: a call's time is the interval between the events around it, so it holds one
+    event marker (about 3 us), as in the main loop's per-path pass."""
     import torch
     for _ in range(3):
         for fn in fns.values():
             fn()
     torch.cuda.synchronize()
     evs = {k: [] for k in fns}
+    marks = [torch.cuda.Event(enable_timing=True)]
+    marks[0].record()
     for _ in range(steps):
         for k, fn in fns.items():
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
             fn()
-            b.record()
-            evs[k].append((a, b))
+            e = torch.cuda.Event(enable_timing=True)
+            e.record()
+            evs[k].append((marks[-1], e))
+            marks.append(e)
     torch.cuda.synchronize()
     res = {}
     for k in fns:
         us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs[k])
         res[k] = us[len(us) // 2]
     return res
+
+
+def time_back_to_back(fn, steps: int, repeats: int = 5) -> float:
+    """Microseconds per call of `fn` called `steps` times back to back between two HIP events (the
+    host enqueues ahead of the GPU, so neither host launch gaps nor per-call markers show); the
+    median over `repeats` such runs."""
+    import torch
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    us = []
+    for _ in range(repeats):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        us.append(a.elapsed_time(b) * 1e3 / steps)
+    us.sort()
+    return us[len(us) // 2]
 
 
 def path_entry(us: float, tokens: int, w) -> dict:
@@ -324,19 +336,7 @@ def measure_sparse(G, rf, d2, qn, qr, E, bt, sl, lens, steps: int, topks=(2048, 
 
         def fn():
             G.gqla_decode_gqa_sparse(d2, qn, qr, E, bt, sl, idx, out, lse=lse, workspace=ws)
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
-        evs = []
-        for _ in range(steps):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            fn()
-            b.record()
-            evs.append((a, b))
-        torch.cuda.synchronize()
-        us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
-        med = us[len(us) // 2]
+        med = time_back_to_back(fn, steps)
         w = rf.work_gqa_sparse(idx_h.numpy(), lens, 128, 8, 64, 128, 128, 2)
         res[f"topk_{topk}"] = {"us_median": med, "tok_s": B * 2 / (med * 1e-6), "alg_bytes": w.bytes,
                                "bound": w.bound(), "achieved_GBps": w.bytes / (med * 1e-6) / 1e9,
@@ -374,19 +374,7 @@ def measure_sparse_ragged(G, rf, config_case, steps: int, topk: int = 2048, spli
         def fn():
             G.gqla_decode_gqa_sparse(d, qn, qr, E, bt, sl, idx, out, lse=lse, workspace=ws,
                                      split_entries=split)
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
-        evs = []
-        for _ in range(steps):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            fn()
-            b.record()
-            evs.append((a, b))
-        torch.cuda.synchronize()
-        us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
-        med = us[len(us) // 2]
+        med = time_back_to_back(fn, steps)
         res[f"split_{split}" if split else "unsplit"] = {
             "us_median": med, "tok_s": B * 2 / (med * 1e-6), "achieved_GBps": w.bytes / (med * 1e-6) / 1e9,
             "roofline_us": w.roofline_us(), "roofline_frac": w.roofline_us() / med}
