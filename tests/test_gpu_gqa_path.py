@@ -151,6 +151,22 @@ def test_gqa_decode_matches_oracle(name, s_q, kw):
     assert_close(f64(out), ex_o, "out vs oracle over GPU-expanded cache", max_rel=8e-3, rel_l2=4e-3)
 
 
+def test_gqa_bench_launch_configuration_full_context():
+    # the bench's GQA call: DeepSeek-V3 shape, batch 64, context 4096, s_q = 2,
+    # unsplit (512 workgroups); sampled sequences against the oracle
+    log("gqa/full size dsv3 B=64 ctx=4096 (sampled sequences)")
+    case = config_case("dsv3", 2)
+    d = dims_of(case)
+    gc = GpuCase(case)
+    E = gc.expand()
+    out, lse = gc.gqa(E)
+    torch.cuda.synchronize()
+    seqs = [0, 31, 63]
+    ref_o, ref_l = decode_literal(*oracle_args(case), d, seqs=seqs)
+    assert_close(f64(out)[seqs], ref_o, "out vs literal oracle")
+    assert_lse_close(f64(lse)[seqs], ref_l, "lse vs literal oracle")
+
+
 @pytest.mark.parametrize("split_tokens", [64, 128, 1024])
 def test_gqa_split_kv_matches_oracle(split_tokens):
     log(f"gqa/split {split_tokens}")

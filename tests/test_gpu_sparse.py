@@ -79,15 +79,18 @@ def test_sparse_matches_oracle(name, s_q, kw, topk, invalid, dup):
 @pytest.mark.parametrize("name,s_q", [("tiny", 2), ("dsv3", 2), ("dsv3", 1)])
 def test_every_position_in_order_equals_the_dense_decode_bitwise(name, s_q):
     # the same tokens land in the same tiles in the same order, and padding
-    # entries are masked exactly as tokens past the end are
+    # entries are masked exactly as tokens past the end are (40 sequences:
+    # more workgroups than CUs, as at the bench's batch)
     log(f"sparse=dense {name} s_q={s_q}")
-    case = config_case(name, s_q, poison=True, table="random", batch=3, ctx=(300, 64, 97))
+    B = 40
+    case = config_case(name, s_q, poison=True, table="random", batch=B,
+                       ctx=tuple((300, 64, 97)[i % 3] for i in range(B)))
     gc = GpuCase(case)
     E = gc.expand()
     L = gc.seqlens_host
     topk = max(L)
-    idx = torch.full((3, gc.d.num_groups, topk), -1, dtype=torch.int32)
-    for b in range(3):
+    idx = torch.full((B, gc.d.num_groups, topk), -1, dtype=torch.int32)
+    for b in range(B):
         idx[b, :, : L[b]] = torch.arange(L[b], dtype=torch.int32)
     out, lse = run_sparse(gc, E, idx)
     dense_o, dense_l = gc.gqa(E)
