@@ -206,3 +206,26 @@ def test_split_sparse_writes_only_its_workspace():
     assert torch.all(wbuf[n_ws:] == 9)
     plan = wbuf[off[1]: off[1] + 4 * (B + 1)].view(torch.int32).cpu().tolist()
     assert plan == [0, 5, 10]                                   # 608 padded entries -> 5 ranges
+
+
+@pytest.mark.parametrize("name,s_q,topk,split,seed", [
+    ("dsv3_ragged", 2, 2048, 512, 2048 + 1),     # the bench's small-batch ragged call, in ranges of 512
+    ("dsv3_ragged", 2, 2048, 1024, 2048 + 1),    # and in ranges of 1024
+    ("dsv3_ragged", 2, 2048, 0, 2048 + 1),       # and unsplit
+    ("dsv3", 2, 512, 0, 512),                    # the bench's batch-64 call at 512 entries per group
+])
+def test_sparse_bench_launches_sampled(name, s_q, topk, split, seed):
+    log(f"sparse/bench launch {name} topk={topk} split={split} (sampled sequences)")
+    case = config_case(name, s_q)
+    d = dims_of(case)
+    gc = GpuCase(case)
+    E = gc.expand()
+    idx = sparse_indices(gc.seqlens_host, d.g, topk, seed=seed)
+    out, lse = run_sparse(gc, E, idx, split=split)
+    torch.cuda.synchronize()
+    L = case.seqlens.numpy()
+    seqs = sorted({0, int(np.argmax(L)), int(np.argmin(L)), len(L) - 1})
+    ex_o, ex_l = decode_gqa_sparse(f64(case.q_nope), f64(case.q_rope), f64(E),
+                                   case.block_table.numpy(), case.seqlens.numpy(), idx.numpy(), d,
+                                   seqs=seqs)
+    check(out[seqs], lse[seqs], ex_o, ex_l, "bench launch sampled", max_rel=8e-3, rel_l2=4e-3)
