@@ -164,7 +164,7 @@ def measure_append(G, d, pages, bt, sl, lens, w_uk, w_uv, E, steps: int, n_new: 
                         "rope slots in the expanded cache (g = 8)", "us_per_call_median": us[len(us) // 2]}
 
 
-def measure_g4(G, rf, config_case, steps: int, absorb_split: int):
+def measure_g4(G, rf, config_case, steps: int, absorb_split: int, gsplit: int = 0):
     """The pages' other ridge-optimal configuration, (g, s_q) = (4, 1): 32 heads per group,
     2176 B per token in the expanded cache; both paths over a 64 x 4096 batch, alternating
     (each path's cache flushes the other's from the 256 MB memory-side cache)."""
@@ -182,12 +182,9 @@ def measure_g4(G, rf, config_case, steps: int, absorb_split: int):
     lse = torch.empty(B, 1, case.h_q, dtype=torch.float32, device=dev)
     sa = G.make_split_plan(lens, absorb_split) + (absorb_split,) if absorb_split else None
     ws = G.absorb_workspace(d, B, total_splits=sa[1] if sa else 0)
-    # GQA: one workgroup per (sequence, group) is only 256 workgroups of two waves here, so the
-    # call is split into 2048-token partitions (512 workgroups) and merged by the combine
-    gsplit = 2048
-    og, tg = G.make_split_plan(lens, gsplit)
-    po = torch.empty(tg, 1, case.h_q, case.d_v, dtype=torch.float32, device=dev)
-    pl = torch.empty(tg, 1, case.h_q, dtype=torch.float32, device=dev)
+    og, tg = G.make_split_plan(lens, gsplit) if gsplit else (None, 0)
+    po = torch.empty(tg, 1, case.h_q, case.d_v, dtype=torch.float32, device=dev) if gsplit else None
+    pl = torch.empty(tg, 1, case.h_q, dtype=torch.float32, device=dev) if gsplit else None
     fns = {
         "mqa_absorb": lambda: G.gqla_decode_mqa_absorb(d, qn, qr, pages, bt, sl, w_uk, w_uv, out=out, lse=lse,
                                                        split_offsets=sa[0] if sa else None,
@@ -570,8 +567,8 @@ def main():
         variants["llama3_8b"] = {
             "workload": "LLaMA-3-8B-shaped layer: 32 query heads, 8 groups, latent 512 + rope 64, nope/v 128, "
                         "batch 32, context 2048; both paths at s_q = 1 and s_q = 2",
-            "absorb_split_tokens": 512, "gqa_split_tokens": 1024,
-            "paths": measure_dense(G, rf, config_case, "llama3_8b", args.steps, 512, 1024, ((1, 1), (2, 2)), 1001)}
+            "absorb_split_tokens": 512, "gqa_split_tokens": 0,
+            "paths": measure_dense(G, rf, config_case, "llama3_8b", args.steps, 512, 0, ((1, 1), (2, 2)), 1001)}
     cpu = None
     parity = None
     if not args.no_cpu and not args.only:

@@ -7,7 +7,11 @@
 //
 // Work decomposition: one workgroup per (split unit, group), one wave per
 // 16-row tile of the group's query rows (h_q/g heads x s_q tokens, padded),
-// which stay in registers.  Each 32-token tile of the group's K and V blocks
+// which stay in registers.  When a launch has at most one workgroup per CU,
+// the workgroup holds two or four such wave groups that take alternate tiles,
+// each with its own running softmax state, merged through LDS at the end (the
+// log-sum-exp merge of split-KV inside the workgroup): a CU then keeps as
+// many waves busy as at two workgroups per CU, with no second launch.  Each 32-token tile of the group's K and V blocks
 // (both token-major) and of the shared rope key is copied HBM -> LDS by direct
 // DMA (global_load_lds_dwordx4, three tiles ahead, no VGPR staging; the waves
 // share the copy instructions and the tile; K and V, read once, with the
@@ -31,12 +35,15 @@
 namespace gqla {
 
 
-template <int HPG, int SQ, int DN, int DV, int DR>
+// NB tile buffers; HV wave groups ("halves"), each of NW waves, taking the
+// tiles it with it % HV == its index and keeping its own softmax state,
+// merged in LDS at the end.
+template <int HPG, int SQ, int DN, int DV, int DR, int NB = 4, int HV = 1>
 struct GqaCfg {
   static constexpr int BS = 64;
   static constexpr int TILE = 32;
-  static constexpr int NBUF = 4;                  // tile buffers
-  static constexpr int LA = NBUF - 1;             // tiles in flight ahead of the one in use
+  static constexpr int NBUF = NB;                 // tile buffers
+  static constexpr int PF = NBUF / HV - 1;        // rounds of HV tiles in flight ahead of the one in use
   static constexpr int ROWS = HPG * SQ;
   static constexpr int NT = (ROWS + 15) / 16;     // 16-row tiles
   static constexpr int KSN = DN / 32;             // 32-wide k steps over d_nope
@@ -52,14 +59,16 @@ struct GqaCfg {
   static constexpr int NI_K = K_BYTES / 1024, NI_V = V_BYTES / 1024;
   static constexpr int NI_R = (R_BYTES + 1023) / 1024;
   static constexpr int NI = NI_K + NI_V + NI_R;   // DMA instructions per tile
-  static constexpr int NW = NT;                   // waves per workgroup, one per 16-row tile
-  static constexpr int NIW = NI / NW;             // DMA instructions per wave per tile
+  static constexpr int NW = NT;                   // waves per wave group, one per 16-row tile
+  static constexpr int NWT = NW * HV;             // waves per workgroup
+  static constexpr int NIW = NI / NW;             // DMA instructions per wave per tile of its group
   static_assert(DN % 32 == 0 && DV % 16 == 0 && DR % 8 == 0, "unsupported head dims");
   static_assert(K_BYTES % 1024 == 0 && V_BYTES % 1024 == 0, "whole DMA instructions");
   static_assert(NI % NW == 0, "the waves share the copies evenly");
-  static_assert(NW <= 4, "launch bound of 256 threads");
-  static_assert(LA * NIW < 64, "vmcnt budget");
-  static_assert(LA <= 3, "the in-flight wait covers up to two later tiles");
+  static_assert(NWT <= 4, "launch bound of 256 threads");
+  static_assert(NBUF % HV == 0 && PF >= 1, "whole rounds of tiles in the ring");
+  static_assert(PF * NIW < 64, "vmcnt budget");
+  static_assert(NBUF * TILE_BYTES <= 160 * 1024, "LDS budget");
   static_assert((KCH & (KCH - 1)) == 0 && (RCH & (RCH - 1)) == 0, "power-of-two rows");
   static_assert(DV == 32 || DV == 64 || DV == 128, "V rows of 64, 128 or 256 bytes");
 };
@@ -132,9 +141,27 @@ __device__ __forceinline__ void dma16_gather(const void* addr, lds_u8_t* lds_bas
 // GQLA"; every query row of the group shares the selection, so the group's
 // rows stay one dense MFMA tile).  Entries are gathered row by row into the
 // same LDS tile layout, so the tile step is the same apart from its masks.
-template <int HPG, int SQ, int DN, int DV, int DR, bool SPARSE>
+// Wait until at most `ahead` tiles of NIW copies each are still in flight
+// (ahead in 0 .. MAXA, wave-uniform).
+template <int NIW, int MAXA>
+__device__ __forceinline__ void wait_tiles_ahead(int ahead) {
+  if constexpr (MAXA > 0) {
+    if (ahead >= MAXA) {
+      vm_wait<MAXA * NIW>();
+      return;
+    }
+    wait_tiles_ahead<NIW, MAXA - 1>(ahead);
+  } else {
+    vm_wait<0>();
+  }
+}
+
+// NB: tile buffers (NB - 1 tiles in flight ahead of the one in use).  Four
+// when two workgroups share a CU; more when a launch has one workgroup per CU,
+// so that a CU keeps about as many bytes in flight either way.
+template <int HPG, int SQ, int DN, int DV, int DR, bool SPARSE, int NB, int HV>
 __global__ __launch_bounds__(256) void gqa_decode_kernel(DecodeParams p) {
-  using C = GqaCfg<HPG, SQ, DN, DV, DR>;
+  using C = GqaCfg<HPG, SQ, DN, DV, DR, NB, HV>;
   constexpr int BS = C::BS, NW = C::NW, KSN = C::KSN, KSR = C::KSR, MT = C::MT;
   constexpr int KCH = C::KCH, RCH = C::RCH, VCH = C::VCH;
   __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[C::NBUF * C::TILE_BYTES];
@@ -153,7 +180,9 @@ __global__ __launch_bounds__(256) void gqa_decode_kernel(DecodeParams p) {
 
   int b, lo, hi;
   const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);   // this wave's 16-row tile
+  const int wid = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int w = wid % NW;                         // this wave's 16-row tile
+  const int hv = wid / NW;                        // its wave group: tiles it with it % HV == hv
   if constexpr (SPARSE) {                         // units: (sequence, entry range) x group
     if (p.split_offsets) {
       b = unit_owner(p.split_offsets, p.seqlens, p.batch, u).b;
@@ -304,7 +333,11 @@ __global__ __launch_bounds__(256) void gqa_decode_kernel(DecodeParams p) {
   // The query loads complete before the first tile copy is issued, so the
   // compiler's own wait tracking has nothing pending inside the tile loop.
   vm_wait<0>();
-  for (int i = 0; i < C::LA && i < n_tiles; ++i) issue_tile(i, codes_of(i));
+  constexpr int PF = C::PF;
+  // this group's tiles: it = HV j + hv, j < n_my; round k holds tiles HV k .. HV k + HV - 1
+  const int n_my = n_tiles > hv ? (n_tiles - hv + HV - 1) / HV : 0;
+  const int n_rounds = (n_tiles + HV - 1) / HV;
+  for (int j = 0; j < PF && j < n_my; ++j) issue_tile(HV * j + hv, codes_of(HV * j + hv));
 
   f32x4 o[MT];
 #pragma unroll
@@ -414,27 +447,63 @@ __global__ __launch_bounds__(256) void gqa_decode_kernel(DecodeParams p) {
     }
   };
 
-  for (int it = 0; it < n_tiles; ++it) {
-    // sparse: the row codes of tile it + LA, read before the wait so their
+  for (int k = 0; k < n_rounds; ++k) {
+    const int it = HV * k + hv;                   // this group's tile of round k (none past the end)
+    const int itn = HV * (k + PF) + hv;           // its tile whose copies this round issues
+    // sparse: the row codes of tile itn, read before the wait so their
     // latency overlaps it (clamped to a real tile; unused past the end)
-    const TileCodes nxt = codes_of(min(it + C::LA, n_tiles - 1));
-    // this wave's copies of tile it landed (those of the next LA-1 tiles may
-    // be in flight); after the barrier every wave's copies of tile it landed
-    // and every wave is done with tile it-1, whose buffer takes tile it+LA
-    const int ahead = min(C::LA - 1, n_tiles - 1 - it);     // later tiles in flight
-    if (ahead == 2) vm_wait<2 * C::NIW>();
-    else if (ahead == 1) vm_wait<C::NIW>();
-    else vm_wait<0>();
-    if constexpr (NW > 1) __syncthreads();
-    if (it + C::LA < n_tiles) issue_tile(it + C::LA, nxt);
-    const lds_u8_t* buf = lds + (it % C::NBUF) * C::TILE_BYTES;
-    const int t0 = lo + C::TILE * it;
-    // only tiles that reach the first causal bound (L - s_q + 1), the last
-    // one or two of the sequence, mask logits and V rows; sparse tiles do
-    // when an entry is invalid or visible to later query rows only
-    const bool edge = SPARSE ? ((edge_bits >> (it % C::NBUF)) & 1) != 0 : (t0 + C::TILE > L - SQ + 1);
-    if (edge) tile_step(buf, t0, std::true_type{});
-    else tile_step(buf, t0, std::false_type{});
+    const TileCodes nxt = codes_of(min(itn, n_tiles - 1));
+    // this wave's copies of tile it landed (those of its next PF - 1 tiles
+    // may be in flight); after the barrier every wave's copies of round k
+    // landed and every wave is done with round k - 1, whose buffers take
+    // round k + PF
+    wait_tiles_ahead<C::NIW, PF - 1>(max(0, min(PF - 1, n_my - 1 - k)));   // later tiles in flight
+    if constexpr (C::NWT > 1) __syncthreads();
+    if (itn < n_tiles) issue_tile(itn, nxt);
+    if (it < n_tiles) {
+      const lds_u8_t* buf = lds + (it % C::NBUF) * C::TILE_BYTES;
+      const int t0 = lo + C::TILE * it;
+      // only tiles that reach the first causal bound (L - s_q + 1), the last
+      // one or two of the sequence, mask logits and V rows; sparse tiles do
+      // when an entry is invalid or visible to later query rows only
+      const bool edge = SPARSE ? ((edge_bits >> (it % C::NBUF)) & 1) != 0 : (t0 + C::TILE > L - SQ + 1);
+      if (edge) tile_step(buf, t0, std::true_type{});
+      else tile_step(buf, t0, std::false_type{});
+    }
+  }
+
+  // The wave groups' states of the same rows meet in LDS (over the tile
+  // ring): group 0 merges them by their row maxima, as the split merge does.
+  if constexpr (HV > 1) {
+    constexpr int NF = 4 * MT + 2;                // floats per lane: o, m_run, l_run
+    __syncthreads();                              // every tile read
+    float* xs = (float*)lds_raw;                  // [group - 1][wave][field][lane]
+    if (hv > 0) {
+      float* dst = xs + ((hv - 1) * NW + w) * NF * 64 + lane;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[(4 * mt + i) * 64] = o[mt][i];
+      dst[(4 * MT) * 64] = m_run;
+      dst[(4 * MT + 1) * 64] = l_run;
+    }
+    __syncthreads();
+    if (hv > 0) return;
+#pragma unroll
+    for (int h2 = 1; h2 < HV; ++h2) {
+      const float* src = xs + ((h2 - 1) * NW + w) * NF * 64 + lane;
+      const float m2 = src[(4 * MT) * 64];
+      const float mn = fmaxf(m_run, m2);
+      if (mn == -INFINITY) continue;              // neither state saw a token of these rows
+      const float a = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mn);
+      const float b2 = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - mn);
+      l_run = l_run * a + src[(4 * MT + 1) * 64] * b2;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[mt][i] = o[mt][i] * a + src[(4 * mt + i) * 64] * b2;
+      m_run = mn;
+    }
   }
 
   // Epilogue: lane (q, c) holds dims 16*mt + 4q .. +3 of row 16 w + c.
@@ -464,14 +533,35 @@ __global__ __launch_bounds__(256) void gqa_decode_kernel(DecodeParams p) {
   }
 }
 
+hipError_t cu_count(int* n);   // compute units of the current device (expand.hip)
+
 // Host-side launcher: returns hipError_t of the launch.
 template <int HPG, int SQ, int DN, int DV, int DR, bool SPARSE>
 hipError_t launch_gqa(const DecodeParams& p, hipStream_t stream) {
   const int g = p.num_groups;
   const int rounds = (p.num_units + 7) / 8;
   const unsigned grid = (unsigned)rounds * 8u * (unsigned)g;
-  hipLaunchKernelGGL((gqa_decode_kernel<HPG, SQ, DN, DV, DR, SPARSE>), dim3(grid),
-                     dim3(64 * GqaCfg<HPG, SQ, DN, DV, DR>::NW), 0, stream, p);
+  using C4 = GqaCfg<HPG, SQ, DN, DV, DR, 4, 1>;
+  constexpr int NW = C4::NW;
+  int cus = 0;
+  const hipError_t e = cu_count(&cus);
+  if (e != hipSuccess) return e;
+  // With at most one workgroup per CU, each (unit, group) workgroup runs
+  // several wave groups over alternate tiles (four one-wave groups, else two),
+  // so a CU keeps as many waves busy as two workgroups would.
+  if (grid <= (unsigned)cus) {
+    if constexpr (NW == 1 && 8 * C4::TILE_BYTES <= 160 * 1024 && C4::NIW < 64) {
+      hipLaunchKernelGGL((gqa_decode_kernel<HPG, SQ, DN, DV, DR, SPARSE, 8, 4>), dim3(grid), dim3(256), 0, stream,
+                         p);
+      return hipGetLastError();
+    } else if constexpr (NW <= 2 && 6 * C4::TILE_BYTES <= 160 * 1024 && 2 * C4::NIW < 64) {
+      hipLaunchKernelGGL((gqa_decode_kernel<HPG, SQ, DN, DV, DR, SPARSE, 6, 2>), dim3(grid), dim3(128 * NW), 0,
+                         stream, p);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((gqa_decode_kernel<HPG, SQ, DN, DV, DR, SPARSE, 4, 1>), dim3(grid), dim3(64 * NW), 0, stream,
+                     p);
   return hipGetLastError();
 }
 
