@@ -562,8 +562,8 @@ def main():
         variants["dense_ragged"] = {
             "workload": "ragged long-context mix: DeepSeek-V3 shape, 16 sequences, contexts log-uniform in "
                         "[1024, 32768], random 64-token page table; absorb s_q = 1 and GQA s_q = 2, split-KV",
-            "absorb_split_tokens": 1280, "gqa_split_tokens": 2048,
-            "paths": measure_dense(G, rf, config_case, "dsv3_ragged", args.steps, 1280, 2048, ((1, 2),), 1004)}
+            "absorb_split_tokens": 1280, "gqa_split_tokens": 2560,
+            "paths": measure_dense(G, rf, config_case, "dsv3_ragged", args.steps, 1280, 2560, ((1, 2),), 1004)}
         variants["llama3_8b"] = {
             "workload": "LLaMA-3-8B-shaped layer: 32 query heads, 8 groups, latent 512 + rope 64, nope/v 128, "
                         "batch 32, context 2048; both paths at s_q = 1 and s_q = 2",

@@ -514,6 +514,7 @@ __global__ __launch_bounds__(512) void absorb_merge_kernel(DecodeParams p) {
   constexpr int NCH = (R / 8 + 63) / 64;            // 8-latent chunks per lane
   static_assert(NR <= 32 && NR % 16 == 0 && NR % NWM == 0, "merge tiling");
   static_assert(MD <= NWM, "one output tile per wave");
+  static_assert(RPW * SC <= 64 && SB < 64, "plan and lse lanes");
   __shared__ __attribute__((aligned(16))) unsigned char sm_raw[2 * NR * STR];
   lds_u8_t* const sm = (lds_u8_t*)sm_raw;
   const int G = blockIdx.y, b0 = (blockIdx.x / RCH) * SB;
@@ -522,16 +523,6 @@ __global__ __launch_bounds__(512) void absorb_merge_kernel(DecodeParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, q = lane >> 4;
-  // W_UV^T[G] operands of this wave's output tile md = w, loaded first so that
-  // they arrive during the merge
-  // (the prologue stores W_UV^T[G] in operand order, so each load is one
-  // contiguous 1 KB block)
-  const uint16_t* WT = p.wuvT + (size_t)G * DV * R;
-  const int md = w < MD ? w : 0;
-  bf16x8 wa[R / 32];
-#pragma unroll
-  for (int kk = 0; kk < R / 32; ++kk) wa[kk] = ld_bf16x8(WT + ((size_t)(md * (R / 32) + kk) * 64 + lane) * 8);
-
   // ---- merge: wave w takes rows w, w + 8, ...; lane l holds latent 8l .. 8l+7
   // of the row (one coalesced 1 KB row per load instruction).  The loads (lse
   // and o_lat) of up to SC splits of all the wave's rows are issued
@@ -540,14 +531,22 @@ __global__ __launch_bounds__(512) void absorb_merge_kernel(DecodeParams p) {
   int s0[RPW], ns[RPW], rowi[RPW], rowh[RPW];
   float m[RPW], wsum[RPW];
   float acc[RPW][NCH][8];
+  // The split plan of the workgroup's sequences in one vector load: lane i
+  // (i <= SB) holds the first unit of sequence b0 + i (the end of the plan
+  // past the batch).  Per-row values are then read from those lanes, so the
+  // loads that depend on the plan wait for one memory round trip only.
+  int offv;
+  {
+    const int bi = min(b0 + min(lane, SB), p.batch);
+    offv = p.split_offsets ? p.split_offsets[bi] : bi;
+  }
 #pragma unroll
   for (int j = 0; j < RPW; ++j) {
     const int rr = w + NWM * j;
     const int b = b0 + rr / RG, lr = lr0 + rr % RG;
     const bool bv = b < p.batch;
-    const int bc = bv ? b : 0;                      // loads stay in bounds, no branch
-    const int o0 = p.split_offsets ? p.split_offsets[bc] : bc;
-    const int o1 = p.split_offsets ? p.split_offsets[bc + 1] : bc + 1;
+    const int o0 = __builtin_amdgcn_readlane(offv, rr / RG);
+    const int o1 = __builtin_amdgcn_readlane(offv, rr / RG + 1);
     rowh[j] = G * HPG + lr / SQ;
     rowi[j] = lr % SQ;
     s0[j] = o0;
@@ -559,12 +558,40 @@ __global__ __launch_bounds__(512) void absorb_merge_kernel(DecodeParams p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[j][cc][e] = 0.f;
   }
+  // W_UV^T[G] operands of this wave's output tile md = w, issued after the
+  // split-plan loads (so that waiting for those does not wait for these) and
+  // before the partials' loads, so that they arrive during the merge (the
+  // prologue stores W_UV^T[G] in operand order, so each load is one
+  // contiguous 1 KB block)
+  const uint16_t* WT = p.wuvT + (size_t)G * DV * R;
+  const int md = w < MD ? w : 0;
+  bf16x8 wa[R / 32];
+#pragma unroll
+  for (int kk = 0; kk < R / 32; ++kk) wa[kk] = ld_bf16x8(WT + ((size_t)(md * (R / 32) + kk) * 64 + lane) * 8);
   int smax = 0;
 #pragma unroll
   for (int j = 0; j < RPW; ++j) smax = max(smax, ns[j]);
   for (int sb = 0; sb < smax; sb += SC) {
     u32x4 v[RPW][SC][NCH];
     float ls[RPW][SC];
+    // the lse of every (row j, split sb + k) of the wave in one vector load:
+    // lane j * SC + k
+    float lsv;
+    {
+      const int jl = lane / SC, kl = lane % SC;
+      int s0l = s0[0], nsl = 0, ril = rowi[0], rhl = rowh[0];
+#pragma unroll
+      for (int jj = 0; jj < RPW; ++jj)
+        if (jl == jj) {
+          s0l = s0[jj];
+          nsl = ns[jj];
+          ril = rowi[jj];
+          rhl = rowh[jj];
+        }
+      const bool have = sb + kl < nsl;             // false on lanes past RPW * SC (nsl = 0)
+      const size_t row = ((size_t)(s0l + (have ? sb + kl : 0)) * SQ + ril) * H + rhl;
+      lsv = have ? p.olse[row] : -INFINITY;
+    }
 #pragma unroll
     for (int j = 0; j < RPW; ++j)
 #pragma unroll
@@ -572,7 +599,7 @@ __global__ __launch_bounds__(512) void absorb_merge_kernel(DecodeParams p) {
         const int s = sb + k;
         const bool have = s < ns[j];
         const size_t row = ((size_t)(s0[j] + (have ? s : 0)) * SQ + rowi[j]) * H + rowh[j];
-        ls[j][k] = have ? p.olse[row] : -INFINITY;
+        ls[j][k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lsv), j * SC + k));
 #pragma unroll
         for (int cc = 0; cc < NCH; ++cc) {
           const int ch = lane + 64 * cc;

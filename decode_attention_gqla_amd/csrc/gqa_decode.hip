@@ -7,11 +7,11 @@
 //
 // Work decomposition: one workgroup per (split unit, group), one wave per
 // 16-row tile of the group's query rows (h_q/g heads x s_q tokens, padded),
-// which stay in registers.  When a launch has at most one workgroup per CU,
-// the workgroup holds two or four such wave groups that take alternate tiles,
-// each with its own running softmax state, merged through LDS at the end (the
-// log-sum-exp merge of split-KV inside the workgroup): a CU then keeps as
-// many waves busy as at two workgroups per CU, with no second launch.  Each 32-token tile of the group's K and V blocks
+// which stay in registers.  When a launch has at most two workgroups per CU,
+// the workgroup holds two such wave groups that take alternate tiles, each
+// with its own running softmax state, merged through LDS at the end (the
+// log-sum-exp merge of split-KV inside the workgroup): a CU then keeps about
+// eight waves busy, with no second launch.  Each 32-token tile of the group's K and V blocks
 // (both token-major) and of the shared rope key is copied HBM -> LDS by direct
 // DMA (global_load_lds_dwordx4, three tiles ahead, no VGPR staging; the waves
 // share the copy instructions and the tile; K and V, read once, with the
@@ -546,17 +546,26 @@ hipError_t launch_gqa(const DecodeParams& p, hipStream_t stream) {
   int cus = 0;
   const hipError_t e = cu_count(&cus);
   if (e != hipSuccess) return e;
-  // With at most one workgroup per CU, each (unit, group) workgroup runs
-  // several wave groups over alternate tiles (four one-wave groups, else two),
-  // so a CU keeps as many waves busy as two workgroups would.
-  if (grid <= (unsigned)cus) {
-    if constexpr (NW == 1 && 8 * C4::TILE_BYTES <= 160 * 1024 && C4::NIW < 64) {
-      hipLaunchKernelGGL((gqa_decode_kernel<HPG, SQ, DN, DV, DR, SPARSE, 8, 4>), dim3(grid), dim3(256), 0, stream,
+  // Wave groups over alternate tiles (two per workgroup) when the launch has
+  // at most two workgroups per CU, so that a CU runs about eight waves:
+  //   * at most one workgroup per CU: one-wave row tiles in an eight-buffer
+  //     ring (three rounds in flight), two-wave row tiles in a six-buffer ring;
+  //   * two per CU: a four-buffer ring (one round in flight).
+  if constexpr (NW <= 2 && 2 * C4::NIW < 64) {
+    if (grid <= (unsigned)cus) {
+      if constexpr (NW == 1 && 8 * C4::TILE_BYTES <= 160 * 1024 && 3 * C4::NIW < 64) {
+        hipLaunchKernelGGL((gqa_decode_kernel<HPG, SQ, DN, DV, DR, SPARSE, 8, 2>), dim3(grid), dim3(128), 0, stream,
+                           p);
+        return hipGetLastError();
+      } else if constexpr (6 * C4::TILE_BYTES <= 160 * 1024) {
+        hipLaunchKernelGGL((gqa_decode_kernel<HPG, SQ, DN, DV, DR, SPARSE, 6, 2>), dim3(grid), dim3(128 * NW), 0,
+                           stream, p);
+        return hipGetLastError();
+      }
+    }
+    if (grid <= 2u * (unsigned)cus) {
+      hipLaunchKernelGGL((gqa_decode_kernel<HPG, SQ, DN, DV, DR, SPARSE, 4, 2>), dim3(grid), dim3(128 * NW), 0, stream,
                          p);
-      return hipGetLastError();
-    } else if constexpr (NW <= 2 && 6 * C4::TILE_BYTES <= 160 * 1024 && 2 * C4::NIW < 64) {
-      hipLaunchKernelGGL((gqa_decode_kernel<HPG, SQ, DN, DV, DR, SPARSE, 6, 2>), dim3(grid), dim3(128 * NW), 0,
-                         stream, p);
       return hipGetLastError();
     }
   }

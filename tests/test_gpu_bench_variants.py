@@ -18,14 +18,14 @@ from tests.oracle_util import dims_of, oracle_args
 pytestmark = pytest.mark.gpu
 
 # (config, s_q, absorb split tokens, GQA split tokens (0: unsplit), seed) as bench.py's variants
-# run them; the unsplit GQA calls of the regrouped and LLaMA-shaped batches have one workgroup per
-# CU and run their wave groups over alternate tiles
+# run them; their GQA calls have at most two workgroups per CU and run two wave groups over alternate
+# tiles
 CASES = [
     ("dsv3_g4", 1, 2048, 0, None),
     ("llama3_8b", 1, 512, 0, 1001 + 10),
     ("llama3_8b", 2, 512, 0, 1001 + 10),
-    ("dsv3_ragged", 1, 1280, 2048, 1004 + 10),
-    ("dsv3_ragged", 2, 1280, 2048, 1004 + 10),
+    ("dsv3_ragged", 1, 1280, 2560, 1004 + 10),
+    ("dsv3_ragged", 2, 1280, 2560, 1004 + 10),
 ]
 
 
