@@ -7,8 +7,8 @@
 //
 // Work decomposition: one workgroup per (split unit, group), one wave per
 // 16-row tile of the group's query rows (h_q/g heads x s_q tokens, padded),
-// which stay in registers.  When a launch has at most two workgroups per CU,
-// the workgroup holds two such wave groups that take alternate tiles, each
+// which stay in registers.  When the group's rows take one or two waves, the
+// workgroup holds two such wave groups that take alternate tiles, each
 // with its own running softmax state, merged through LDS at the end (the
 // log-sum-exp merge of split-KV inside the workgroup): a CU then keeps about
 // eight waves busy, with no second launch.  Each 32-token tile of the group's K and V blocks
@@ -546,11 +546,11 @@ hipError_t launch_gqa(const DecodeParams& p, hipStream_t stream) {
   int cus = 0;
   const hipError_t e = cu_count(&cus);
   if (e != hipSuccess) return e;
-  // Wave groups over alternate tiles (two per workgroup) when the launch has
-  // at most two workgroups per CU, so that a CU runs about eight waves:
+  // Two wave groups over alternate tiles per workgroup when the row tiles
+  // take at most two waves, so that a CU runs about eight waves:
   //   * at most one workgroup per CU: one-wave row tiles in an eight-buffer
   //     ring (three rounds in flight), two-wave row tiles in a six-buffer ring;
-  //   * two per CU: a four-buffer ring (one round in flight).
+  //   * more: a four-buffer ring (one round in flight), two workgroups per CU.
   if constexpr (NW <= 2 && 2 * C4::NIW < 64) {
     if (grid <= (unsigned)cus) {
       if constexpr (NW == 1 && 8 * C4::TILE_BYTES <= 160 * 1024 && 3 * C4::NIW < 64) {
@@ -563,11 +563,9 @@ hipError_t launch_gqa(const DecodeParams& p, hipStream_t stream) {
         return hipGetLastError();
       }
     }
-    if (grid <= 2u * (unsigned)cus) {
-      hipLaunchKernelGGL((gqa_decode_kernel<HPG, SQ, DN, DV, DR, SPARSE, 4, 2>), dim3(grid), dim3(128 * NW), 0, stream,
-                         p);
-      return hipGetLastError();
-    }
+    hipLaunchKernelGGL((gqa_decode_kernel<HPG, SQ, DN, DV, DR, SPARSE, 4, 2>), dim3(grid), dim3(128 * NW), 0, stream,
+                       p);
+    return hipGetLastError();
   }
   hipLaunchKernelGGL((gqa_decode_kernel<HPG, SQ, DN, DV, DR, SPARSE, 4, 1>), dim3(grid), dim3(64 * NW), 0, stream,
                      p);
