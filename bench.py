@@ -145,9 +145,7 @@ def measure_append(G, d, pages, bt, sl, lens, w_uk, w_uv, E, steps: int, n_new: 
     sl_ = torch.tensor([s for _, s in idx], device="cuda")
     rows = pages[pg, sl_].reshape(B, n_new, -1).contiguous()
     fn = lambda: G.gqla_append_tokens(d, rows, pages, bt, sl, w_uk, w_uv, expanded_pages=E)
-    for _ in range(3):
-        fn()
-    torch.cuda.synchronize()
+    warm_up(fn)
     # back-to-back calls between two events (the host enqueues ahead, so launch overhead on the
     # host does not show), several repeats
     us = []
@@ -208,16 +206,32 @@ def measure_g4(G, rf, config_case, steps: int, absorb_split: int, gsplit: int = 
             "gqa_split_tokens": gsplit, "paths": res}
 
 
+def warm_up(fn, seconds: float = 0.05):
+    """Call `fn` for about `seconds` of GPU time before timing it: the GPU reaches its steady
+    clock only after some tens of milliseconds of work (the main loop's 200 warmup steps take
+    about 50 ms), and a variant's calls follow seconds of host-side input generation."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(3):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    per_call = max(a.elapsed_time(b) * 1e-3 / 3, 1e-6)
+    for _ in range(min(2000, int(seconds / per_call))):
+        fn()
+    torch.cuda.synchronize()
+
+
 def time_alternating(fns: dict, steps: int) -> dict:
     """Median microseconds per call of each function, calling them in turn (each path's cache then
     flushes the other's from the 256 MB memory-side cache, as in a step).  One HIP event between
     consecutive calls: a call's time is the interval between the events around it, so it holds one
     event marker (about 3 us), as in the main loop's per-path pass."""
     import torch
-    for _ in range(3):
-        for fn in fns.values():
-            fn()
-    torch.cuda.synchronize()
+    warm_up(lambda: [fn() for fn in fns.values()])
     evs = {k: [] for k in fns}
     marks = [torch.cuda.Event(enable_timing=True)]
     marks[0].record()
@@ -241,9 +255,7 @@ def time_back_to_back(fn, steps: int, repeats: int = 5) -> float:
     host enqueues ahead of the GPU, so neither host launch gaps nor per-call markers show); the
     median over `repeats` such runs."""
     import torch
-    for _ in range(3):
-        fn()
-    torch.cuda.synchronize()
+    warm_up(fn)
     us = []
     for _ in range(repeats):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
