@@ -477,9 +477,10 @@ __global__ __launch_bounds__(256) void gqa_decode_kernel(DecodeParams p) {
   if constexpr (HV > 1) {
     constexpr int NF = 4 * MT + 2;                // floats per lane: o, m_run, l_run
     __syncthreads();                              // every tile read
-    float* xs = (float*)lds_raw;                  // [group - 1][wave][field][lane]
+    typedef __attribute__((address_space(3))) float lds_f32_t;
+    lds_f32_t* const xs = (lds_f32_t*)lds;        // [group - 1][wave][field][lane]
     if (hv > 0) {
-      float* dst = xs + ((hv - 1) * NW + w) * NF * 64 + lane;
+      lds_f32_t* dst = xs + ((hv - 1) * NW + w) * NF * 64 + lane;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -491,7 +492,7 @@ __global__ __launch_bounds__(256) void gqa_decode_kernel(DecodeParams p) {
     if (hv > 0) return;
 #pragma unroll
     for (int h2 = 1; h2 < HV; ++h2) {
-      const float* src = xs + ((h2 - 1) * NW + w) * NF * 64 + lane;
+      const lds_f32_t* src = xs + ((h2 - 1) * NW + w) * NF * 64 + lane;
       const float m2 = src[(4 * MT) * 64];
       const float mn = fmaxf(m_run, m2);
       if (mn == -INFINITY) continue;              // neither state saw a token of these rows
