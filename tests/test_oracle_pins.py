@@ -373,6 +373,27 @@ def test_expansion_with_selection_weights_is_a_pure_gather():
                 assert E[p, expanded_offset_rope(d, s, j)] == pages_bf[p, s, d.r + j]
 
 
+def test_expanded_values_are_bf16_within_half_an_ulp_of_the_exact_product():
+    # The expansion stores each K and V element once in bf16: every stored value must be a bf16
+    # number (its 8 significant bits and nothing below), and it must lie within half a bf16 ulp
+    # of the exact product c_t . W[G][:, j], summed here term by term.
+    case = tiny_case((20, 9), 1, seed=85)
+    d = dims_of(case)
+    _, _, pages, _, _, w_uk, w_uv = oracle_args(case)
+    E = expand_pages(pages, w_uk, w_uv, d)
+    for p in range(pages.shape[0]):
+        for G in range(d.g):
+            for s in range(d.bs):
+                for w, off, n in ((w_uk, expanded_offset_k, d.d_nope), (w_uv, expanded_offset_v, d.d_v)):
+                    for j in range(n):
+                        got = E[p, off(d, G, s, j)]
+                        exact = math.fsum(pages[p, s, k] * w[G, k, j] for k in range(d.r))
+                        m, e = math.frexp(got)                      # got = m * 2**e, |m| in [0.5, 1)
+                        assert m * 256 == int(m * 256)               # 8 significant bits
+                        half_ulp = math.ldexp(1.0, math.frexp(exact)[1] - 9) if exact else 0.0
+                        assert abs(got - exact) <= half_ulp
+
+
 @pytest.mark.parametrize("s_q", [1, 2])
 def test_gqa_over_expanded_cache_equals_literal_up_to_bf16_storage(s_q):
     case = tiny_case((40, 66), s_q, seed=91 + s_q)

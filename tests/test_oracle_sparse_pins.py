@@ -107,9 +107,9 @@ def test_list_order_padding_and_duplicates():
     # order of the list is irrelevant
     o_p, l_p = decode_gqa_sparse(qn, qr, E, bt, sl, idx[:, :, ::-1], d)
     assert rel(o_p, o) < 1e-12 and np.max(np.abs(l_p - l)) < 1e-12
-    # -1 and positions >= L are ignored
-    pad = np.concatenate([idx, np.full_like(idx, -1), idx * 0 + np.asarray(sl)[:, None, None] + 3],
-                         axis=2)
+    # -1 and positions >= L (L itself, the first position past the context, and L + 3) are ignored
+    past = idx * 0 + np.asarray(sl)[:, None, None]
+    pad = np.concatenate([idx, np.full_like(idx, -1), past, past + 3], axis=2)
     o_x, l_x = decode_gqa_sparse(qn, qr, E, bt, sl, pad, d)
     assert rel(o_x, o) < 1e-12 and np.max(np.abs(l_x - l)) < 1e-12
     # every entry listed twice: same weights, the sum of exponentials doubles
