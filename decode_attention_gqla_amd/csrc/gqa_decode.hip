@@ -8,16 +8,17 @@
 // Work decomposition: one workgroup per (split unit, group), one wave per
 // 16-row tile of the group's query rows (h_q/g heads x s_q tokens, padded),
 // which stay in registers.  When the group's rows take one or two waves, the
-// workgroup holds two such wave groups that take alternate tiles, each
-// with its own running softmax state, merged through LDS at the end (the
+// workgroup holds two such wave groups that take alternate tiles, each with
+// its own running softmax state, merged through LDS at the end (the
 // log-sum-exp merge of split-KV inside the workgroup): a CU then keeps about
-// eight waves busy, with no second launch.  Each 32-token tile of the group's K and V blocks
-// (both token-major) and of the shared rope key is copied HBM -> LDS by direct
-// DMA (global_load_lds_dwordx4, three tiles ahead, no VGPR staging; the waves
-// share the copy instructions and the tile; K and V, read once, with the
-// non-temporal policy, the rope tile shared by the g group workgroups through
-// L2 without it), then read as bf16 MFMA operands (the copies are waited for
-// explicitly with vmcnt, see dma16):
+// eight waves busy, with no second launch.  Each 32-token tile of the group's
+// K and V blocks (both token-major) and of the shared rope key is copied
+// HBM -> LDS by direct DMA (global_load_lds_dwordx4 into a ring of 4, 6 or 8
+// tile buffers, no VGPR staging; the waves of a wave group share the copy
+// instructions of its tiles; K and V, read once, with the non-temporal
+// policy, the rope tile shared by the g group workgroups through L2 without
+// it), then read as bf16 MFMA operands (the copies are waited for explicitly
+// with vmcnt, see dma16):
 //   S^T[token][row] = K[token][:] . Q[row][:]        (A = cache rows, B = Q^T)
 //   O^T[dim][row]  += V^T[dim][token] . P^T[token][row]
 // The token order inside a tile is relabelled so that the S^T accumulator lane
