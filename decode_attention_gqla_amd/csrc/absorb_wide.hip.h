@@ -52,10 +52,20 @@ __device__ __forceinline__ void dma4(const void* base, uint32_t voff_bytes, lds_
 // The 16-byte copy without a memory clobber: it writes only an LDS buffer no
 // wave reads before the next vm_wait + barrier (both of which are ordered
 // against every LDS access), so LDS reads of other buffers may move across it.
+// NT: the non-temporal policy, for a latent cache larger than the
+// memory-side cache (each tile is read by the two row blocks of its unit,
+// which run side by side on one XCD, and by no one else in the call).  A
+// cache that fits keeps the default policy, so that it can stay resident
+// from one decode step to the next.
+template <bool NT>
 __device__ __forceinline__ void dma16_free(const void* base, uint32_t voff_bytes, lds_u8_t* lds_base) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff_bytes), "s"(base), "s"(m0v) : "m0");
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                 :: "v"(voff_bytes), "s"(base), "s"(m0v) : "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff_bytes), "s"(base), "s"(m0v) : "m0");
 }
 
 template <int HPG, int SQ, int R, int DR, int QC>
@@ -107,7 +117,7 @@ struct WideCfg {
 // P % CHR = logical chunk (P % CHR) ^ f(token).  The per-lane source offsets
 // (bytes from the tile's first row, each below 2^16) are packed two per
 // register.
-template <int NC, int CHR>
+template <int NC, int CHR, bool NT>
 struct TileCopier {
   uint32_t dvp[NC > 0 ? (NC + 1) / 2 : 1];
   int k0;
@@ -126,7 +136,7 @@ struct TileCopier {
   }
   // copy instruction kk of this wave's share; tile = the tile's first row
   __device__ __forceinline__ void part(const uint16_t* tile, lds_u8_t* buf, int kk) const {
-    dma16_free(tile, off(kk), buf + (k0 + kk) * 1024);
+    dma16_free<NT>(tile, off(kk), buf + (k0 + kk) * 1024);
   }
   __device__ __forceinline__ void all(const uint16_t* tile, lds_u8_t* buf) const {
 #pragma unroll
@@ -143,7 +153,7 @@ struct TileCopier {
 // PG_LDS: the unit's block-table entries (at most PG_MAX) are copied into LDS
 // at the start and read from there (otherwise by scalar loads, whose waits
 // also drain the LDS reads in flight).
-template <int HPG, int SQ, int R, int DR, int QC, bool PG_LDS>
+template <int HPG, int SQ, int R, int DR, int QC, bool PG_LDS, bool NTC>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void absorb_decode_kernel(DecodeParams p) {
   using C = WideCfg<HPG, SQ, R, DR, QC>;
@@ -207,7 +217,7 @@ void absorb_decode_kernel(DecodeParams p) {
       const int r = P / CHR, pos = P % CHR;
       const int rq = rb * C::ROWS_WG + r;
       const uint32_t off = (uint32_t)(((rq % SQ) * H + rq / SQ) * ROW + ((pos ^ tile_swz(r)) * 8)) * 2u;
-      dma16_free(qbase, off, lds + C::OFF_Q + (w + NW * kk) * 1024);
+      dma16_free<false>(qbase, off, lds + C::OFF_Q + (w + NW * kk) * 1024);
     }
   };
   // Block-table entries of the unit: with PG_LDS every wave copies all of them
@@ -282,7 +292,7 @@ void absorb_decode_kernel(DecodeParams p) {
     float m_ref[2] = {-INFINITY, -INFINITY};
     float l_run[2] = {0.f, 0.f};                   // this lane's share of the sums of rows (rt, c)
     bf16x8 qb[2][KQ];                              // B operands: Q[row 32 rh + 16 rt + c][32 ks + 8 qq ..]
-    TileCopier<NQC, CHR> cp_q;                     // this wave's copy instructions of every tile
+    TileCopier<NQC, CHR, NTC> cp_q;                     // this wave's copy instructions of every tile
     cp_q.init(w * NQC, lane);
 
     // S^T of tile it: s[rt][e] = logit of token 16 th + 4 qq + e of the tile
@@ -485,7 +495,7 @@ void absorb_decode_kernel(DecodeParams p) {
   } else {
     // ================================ PV waves ================================
     const int v = w - NQW;
-    TileCopier<NPC, CHR> cp_p;                     // this wave's copy instructions of every tile
+    TileCopier<NPC, CHR, NTC> cp_p;                     // this wave's copy instructions of every tile
     cp_p.init(NQW * NQC + v * NPC, lane);
     auto zero_tail = [&](int it) {                // latent part only: the PV product reads no rope
       const int valid = L - (lo + C::TILE * it);
@@ -680,6 +690,9 @@ void absorb_decode_kernel(DecodeParams p) {
   }
 }
 
+// Memory-side (Infinity) cache of the MI355X.
+constexpr double kMallBytes = 256.0 * 1024 * 1024;
+
 template <int HPG, int SQ, int R, int DR, int QC>
 hipError_t launch_absorb_wide(const DecodeParams& p, hipStream_t stream) {
   using C = WideCfg<HPG, SQ, R, DR, QC>;
@@ -688,10 +701,19 @@ hipError_t launch_absorb_wide(const DecodeParams& p, hipStream_t stream) {
   const unsigned grid = (unsigned)((p.num_units + 7) / 8) * 8u * (unsigned)RB;
   // block-table entries one unit can span: a split's share, else a whole row
   const long unit_pages = p.split_offsets ? (long)p.split_tokens / C::BS : (long)p.max_blocks;
-  if (unit_pages <= C::PG_MAX)
-    hipLaunchKernelGGL((absorb_decode_kernel<HPG, SQ, R, DR, QC, true>), dim3(grid), dim3(64 * C::NW), 0, stream, p);
-  else
-    hipLaunchKernelGGL((absorb_decode_kernel<HPG, SQ, R, DR, QC, false>), dim3(grid), dim3(64 * C::NW), 0, stream, p);
+  // latent bytes the call can read (units x their longest span): the
+  // non-temporal copies when that exceeds the memory-side cache
+  const double span_tokens = p.split_offsets ? (double)p.num_units * p.split_tokens
+                                             : (double)p.batch * p.max_blocks * C::BS;
+  const bool nt = span_tokens * C::ROW * 2.0 > kMallBytes;
+  const dim3 g3(grid), b3(64 * C::NW);
+  if (unit_pages <= C::PG_MAX) {
+    if (nt) hipLaunchKernelGGL((absorb_decode_kernel<HPG, SQ, R, DR, QC, true, true>), g3, b3, 0, stream, p);
+    else hipLaunchKernelGGL((absorb_decode_kernel<HPG, SQ, R, DR, QC, true, false>), g3, b3, 0, stream, p);
+  } else {
+    if (nt) hipLaunchKernelGGL((absorb_decode_kernel<HPG, SQ, R, DR, QC, false, true>), g3, b3, 0, stream, p);
+    else hipLaunchKernelGGL((absorb_decode_kernel<HPG, SQ, R, DR, QC, false, false>), g3, b3, 0, stream, p);
+  }
   return hipGetLastError();
 }
 
