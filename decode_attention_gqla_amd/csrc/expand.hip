@@ -176,6 +176,9 @@ __device__ __forceinline__ void expand_body(const ExpandParams& p, int64_t tile,
 //     in one burst per block.
 //   * The copy and store instructions of a phase sit between its MFMAs (one
 //     every four), where their issue overlaps the matrix work.
+//   * The latent rows (read once) and the output rows (written once, 1.1 GB
+//     for the DeepSeek-V3-shaped pool) use the non-temporal policy; the weight
+//     slices, shared by every workgroup through L2, the default one.
 template <int R, int DH, int DR>
 struct ExpandPagesCfg {
   static constexpr int BS = 64;
@@ -282,7 +285,9 @@ void expand_pages_kernel(ExpandParams p) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) cb[nt][kc] = ld_bf16x8(crow + (size_t)16 * nt * ROW + 32 * kc);
+      for (int kc = 0; kc < KC; ++kc)
+        cb[nt][kc] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                                                    crow + (size_t)16 * nt * ROW + 32 * kc)));
   }
 #pragma unroll
   for (int j = 0; j < 3; ++j)
@@ -325,7 +330,7 @@ void expand_pages_kernel(ExpandParams p) {
     return *(const lds_u32x4_t*)(stage + stage_off(8 * i + lane / 8, lane % 8));
   };
   auto store_row8 = [&](uint16_t* ob, int i, const u32x4& v) {
-    *reinterpret_cast<u32x4*>(ob + (size_t)(8 * i + lane / 8) * DH + 8 * (lane % 8)) = v;
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(ob + (size_t)(8 * i + lane / 8) * DH + 8 * (lane % 8)));
   };
   // Phase pi (k step kh of pass ps): the MFMAs of slice pi, with the copies
   // of slice pi + 3 (cpy; its buffer was last read in phase pi - 1) and part
